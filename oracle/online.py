@@ -1,0 +1,57 @@
+"""The online-softmax recurrence, in float64 (test infrastructure).
+
+This is the one-pass method the pages build (page 1 section 4, "online softmax
+three-piece set"; page 3 section 1.2 figure 1-A steps 3-7 and section 5
+figure 5): K/V are visited in blocks of ``block_n`` keys while each query row
+keeps a running max m, a running exp-sum l and an accumulator acc.  For each
+key block:
+
+    m_new = max(m, rowmax(S_block))
+    p     = exp(S_block - m_new)
+    alpha = exp(m - m_new)
+    l     = alpha * l + rowsum(p)
+    acc   = alpha * acc + p @ V_block
+    m     = m_new
+
+and at the end O = acc / l and lse = m + ln l.  m starts at -inf, l and acc at
+zero (page 1's initial values).  A final partial block simply holds fewer keys,
+which is what masking padded keys to -inf achieves (page 4's softmax kernel
+pads with -inf so that exp of a pad is zero).
+
+In exact arithmetic this equals the two-pass definition in ``definition``; the
+oracle tests use it only to pin that invariant, for several block sizes,
+including sizes that do not divide N.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def attention_online(q, k, v, scale: float, block_n: int):
+    """O, lse for q, k, v [B, H, N, d] via the blockwise online recurrence."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if block_n < 1:
+        raise ValueError("block_n must be >= 1")
+    B, H, N, _ = q.shape
+    o = np.empty(v.shape, dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = q[b, h], k[b, h], v[b, h]
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            acc = np.zeros((N, vh.shape[1]))
+            for j0 in range(0, N, block_n):
+                j1 = min(N, j0 + block_n)
+                s = float(scale) * (qh @ kh[j0:j1].T)
+                m_new = np.maximum(m, s.max(axis=1))
+                p = np.exp(s - m_new[:, None])
+                alpha = np.exp(m - m_new)
+                l = alpha * l + p.sum(axis=1)
+                acc = alpha[:, None] * acc + p @ vh[j0:j1]
+                m = m_new
+            o[b, h] = acc / l[:, None]
+            lse[b, h] = m + np.log(l)
+    return o, lse

@@ -1,0 +1,149 @@
+"""attention_attn_fwd_07_amd - fused attention forward on MI355X (gfx950).
+
+A thin ctypes binding over ``libattn_fwd.so`` (declared in
+``include/attn_fwd.h``).  It only marshals arguments: torch supplies device
+memory and the current HIP stream, every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if the library is missing, or no
+GPU is present, calls raise.
+
+    o, lse = fwd(q, k, v)                  # allocate outputs, scale = 1/sqrt(d)
+    attn_fwd(q, k, v, o, lse, scale)       # caller-owned outputs, async launch
+
+Tensors are ``[B, H, N, d]`` contiguous, fp32/fp16/bf16, d in {64, 128};
+``lse`` is ``[B, H, N]`` fp32 (or None).  Argument errors raise ValueError,
+mirroring a wrapper that checks device, shape, dtype and contiguity before it
+launches anything (page 2 "Triton programming template", Python wrapper).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from .build import LIB
+
+__all__ = ["attn_fwd", "fwd", "attn_strerror", "attn_version", "library_path", "AttnError"]
+
+ATTN_OK = 0
+ATTN_ERR_HIP = -8
+
+
+class AttnError(ValueError):
+    """An argument error reported by the library (a negative return code)."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"attn_fwd error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        raise ImportError(
+            f"{LIB} is not built; run `python -m attention_attn_fwd_07_amd.build` "
+            "(the HIP library is required: there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                             ctypes.c_int, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_strerror.argtypes = [ctypes.c_int]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def attn_strerror(code: int) -> str:
+    return _load().attn_strerror(int(code)).decode()
+
+
+def attn_version() -> int:
+    return int(_load().attn_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_codes():
+    torch = _torch()
+    return {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+def _check(q, k, v, o, lse):
+    torch = _torch()
+    codes = _dtype_codes()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape == o.shape):
+        raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} "
+                         f"v{tuple(v.shape)} o{tuple(o.shape)}")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise ValueError("q, k, v and o must share one dtype")
+    if q.dtype not in codes:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if not (q.device == k.device == v.device == o.device):
+        raise ValueError("q, k, v and o must be on the same device")
+    if lse is not None:
+        if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32:
+            raise ValueError("lse must be a float32 tensor or None")
+        if lse.device != q.device or not lse.is_contiguous():
+            raise ValueError("lse must be contiguous and on q's device")
+        if tuple(lse.shape) != tuple(q.shape[:3]):
+            raise ValueError(f"lse must have shape {tuple(q.shape[:3])}")
+    return codes[q.dtype]
+
+
+def attn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
+    """O = softmax(scale * Q K^T) V into ``o`` (and the log-sum-exp into ``lse``).
+
+    Asynchronous on ``stream`` (default: torch's current stream of q's device).
+    """
+    torch = _torch()
+    code_dtype = _check(q, k, v, o, lse)
+    B, H, N, d = (int(x) for x in q.shape)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    lib = _load()
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                          ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+                          ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                          B, H, N, d, float(scale), code_dtype, ctypes.c_void_p(stream))
+    if rc == ATTN_ERR_HIP:
+        raise RuntimeError(f"attn_fwd: {attn_strerror(rc)}")
+    if rc != ATTN_OK:
+        raise AttnError(rc, attn_strerror(rc))
+
+
+def fwd(q, k, v, scale: float | None = None, return_lse: bool = True):
+    """Allocate O (and lse) and run ``attn_fwd``; scale defaults to 1/sqrt(d)."""
+    torch = _torch()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = (torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+           if return_lse else None)
+    attn_fwd(q, k, v, o, lse, scale)
+    return o, lse

@@ -1,0 +1,639 @@
+// attn_fwd.hip - fused attention forward for AMD MI355X (gfx950, CDNA4).
+//
+// Method: page 1 "Triton hand-written kernels: from vector add to the
+// FlashAttention core", section 4 (online softmax: running max m, running
+// exp-sum l, rescaled accumulator), and page 3 "OpenAI Triton from
+// introduction to model practice", section 5 (the same forward with a
+// (batch, head, query-block) grid and a log-sum-exp output), figure 1-A's
+// seven steps.  The pages' kernels are Triton programs for NVIDIA parts; this
+// file is a gfx950 design of the same computation.
+//
+// Work unit: one block = 4 wave64s = 128 query rows of one (b, h); each wave
+// owns 32 query rows for the whole key loop.  Key/value tiles of 64 rows are
+// double-buffered through LDS.
+//
+// Register layouts (the core of the design).  With the 32x32xK MFMA, the C/D
+// fragment of lane l holds column (l % 32) and rows 8*(r/4) + 4*(l/32) + r%4
+// for r = 0..15.  The kernel therefore computes the TRANSPOSED scores
+//     S^T[key, query] = K * Q^T            (A = K rows, B = Q rows)
+// so that lane l holds ONE query row (l % 32) and 16 keys per 32-key block.
+// Consequences:
+//   * row max / row sum are in-lane reductions plus one exchange with lane
+//     l ^ 32 (v_permlane32_swap);
+//   * the probabilities P, packed in register order, are already the B
+//     operand of the second product, computed as O^T = V^T * P^T;
+//   * O^T's C fragment again puts query (l % 32) in lane l, so the per-row
+//     rescale by alpha needs no cross-lane traffic;
+//   * V^T's A operand needs 4 consecutive keys of one column per register
+//     pair: exactly what the gfx950 transposing LDS read ds_read_b64_tr_b16
+//     returns from a row-major V tile.
+// An MFMA pairs A-slot t of lane half h with B-slot t of the same half, so
+// any consistent assignment of the contraction index to (half, slot) is
+// correct; the kernel uses contiguous 8-element d runs for Q.K and the
+// C-fragment key order for P.V.
+//
+// Softmax runs in the log2 domain: t = s * (scale * log2 e), p = 2^(t - m),
+// v_exp_f32 computes 2^x; lse is converted back to natural log at the end.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_fwd.h"
+
+namespace {
+
+typedef unsigned int u32;
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kXcds = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kThreads = 256; // 4 wave64s per block
+
+// ---------------------------------------------------------------------------
+// element traits for the 16-bit paths
+// ---------------------------------------------------------------------------
+struct Bf16T {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Two fp32 -> two bf16, round to nearest even (v_cvt_pk_bf16_f32).
+  static __device__ __forceinline__ u32 pack2(float lo, float hi) {
+    return __builtin_bit_cast(u32, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+  }
+};
+
+struct F16T {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // Two fp32 -> two fp16, round to nearest even.
+  static __device__ __forceinline__ u32 pack2(float lo, float hi) {
+    return __builtin_bit_cast(u32, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// shared helpers
+// ---------------------------------------------------------------------------
+
+// Map the hardware block index to a logical tile so that each XCD (own L2)
+// receives one contiguous range of tiles: consecutive tiles are query blocks
+// of the same head, which read the same K/V.  Bijective for any count.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int q = nb / kXcds, r = nb % kXcds;
+  const int x = b % kXcds, i = b / kXcds;
+  return x * q + (x < r ? x : r) + i;
+}
+
+// Value held by lane l ^ 32, combined with the lane's own by op.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xhalf_min(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row extreme over a lane's 16-value fragment.
+__device__ __forceinline__ float frag_max(const f32x16& s) {
+  float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+  float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  float c = fmaxf(fmaxf(s[6], s[7]), s[8]);
+  float d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
+}
+__device__ __forceinline__ float frag_min(const f32x16& s) {
+  float a = fminf(fminf(s[0], s[1]), s[2]);
+  float b = fminf(fminf(s[3], s[4]), s[5]);
+  float c = fminf(fminf(s[6], s[7]), s[8]);
+  float d = fminf(fminf(s[9], s[10]), s[11]);
+  float e = fminf(fminf(s[12], s[13]), s[14]);
+  return fminf(fminf(fminf(a, b), fminf(c, d)), fminf(e, s[15]));
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 kernel
+// ---------------------------------------------------------------------------
+template <int D>
+struct Geo16 {
+  static constexpr int BM = 128;               // query rows per block
+  static constexpr int BN = 64;                // keys per LDS tile
+  static constexpr int ROWB = D * 2;           // bytes per K/V row
+  static constexpr int CH = D / 8;             // 16-byte chunks per row
+  static constexpr int TILEB = BN * ROWB;      // bytes of one K or V tile
+  static constexpr int CPT = BN * CH / kThreads;  // chunks each thread moves
+  static constexpr int KS = D / 16;            // k-steps of K*Q^T
+  static constexpr int DB = D / 32;            // 32-wide column blocks of O
+  static constexpr int SMEM = 4 * TILEB;       // K,V x 2 buffers
+};
+
+// LDS swizzles: physical 16-byte chunk = logical chunk ^ f(row).
+//  K is read as 16-byte rows fragments by 32 lanes of distinct rows: XOR the
+//  chunk with the row so that consecutive rows hit distinct banks.
+//  V is read by ds_read_b64_tr_b16 as 8 rows x 64 bytes per wave: XOR bits 2-3
+//  of the chunk so that the 8 rows spread over the whole bank range.
+template <int D> __device__ __forceinline__ int swz_k(int row);
+template <> __device__ __forceinline__ int swz_k<128>(int row) { return row & 15; }
+template <> __device__ __forceinline__ int swz_k<64>(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+template <int D> __device__ __forceinline__ int swz_v(int row);
+template <> __device__ __forceinline__ int swz_v<128>(int row) { return (row & 3) << 2; }
+template <> __device__ __forceinline__ int swz_v<64>(int row) { return ((row >> 1) & 1) << 2; }
+
+template <int D>
+__device__ __forceinline__ void load_kv_regs(const uint16_t* __restrict__ Kh,
+                                             const uint16_t* __restrict__ Vh, int j0, int N,
+                                             u32x4 (&kr)[Geo16<D>::CPT],
+                                             u32x4 (&vr)[Geo16<D>::CPT]) {
+  using G = Geo16<D>;
+#pragma unroll
+  for (int u = 0; u < G::CPT; ++u) {
+    const int ci = threadIdx.x + u * kThreads;
+    const int row = ci / G::CH, c = ci % G::CH;
+    if (j0 + row < N) {
+      const size_t off = (size_t)(j0 + row) * D + c * 8;
+      kr[u] = *reinterpret_cast<const u32x4*>(Kh + off);
+      vr[u] = *reinterpret_cast<const u32x4*>(Vh + off);
+    } else {  // padded key rows: zeros, so P (=0) * V stays 0
+      kr[u] = (u32x4){0u, 0u, 0u, 0u};
+      vr[u] = (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_kv_lds(unsigned char* kb, unsigned char* vb,
+                                             const u32x4 (&kr)[Geo16<D>::CPT],
+                                             const u32x4 (&vr)[Geo16<D>::CPT]) {
+  using G = Geo16<D>;
+#pragma unroll
+  for (int u = 0; u < G::CPT; ++u) {
+    const int ci = threadIdx.x + u * kThreads;
+    const int row = ci / G::CH, c = ci % G::CH;
+    *reinterpret_cast<u32x4*>(kb + row * G::ROWB + ((c ^ swz_k<D>(row)) << 4)) = kr[u];
+    *reinterpret_cast<u32x4*>(vb + row * G::ROWB + ((c ^ swz_v<D>(row)) << 4)) = vr[u];
+  }
+}
+
+// One K/V tile: scores, online-softmax update, P.V accumulate.
+template <class E, int D, bool TAIL>
+__device__ __forceinline__ void tile_step16(const unsigned char* kb, const unsigned char* vb,
+                                            const u32x4 (&qf)[Geo16<D>::KS],
+                                            f32x16 (&acc)[Geo16<D>::DB], float& m, float& l,
+                                            int j0, int N, float c2) {
+  using G = Geo16<D>;
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 31, hh = lane >> 5;
+
+  // S^T = K Q^T for two 32-key halves of the tile.
+  f32x16 s[2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    s[sb] = (f32x16){};
+    const int row = sb * 32 + li;
+    const unsigned char* rp = kb + row * G::ROWB;
+    const int sw = swz_k<D>(row);
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(rp + (((2 * ks + hh) ^ sw) << 4));
+      s[sb] = E::mfma(a, qf[ks], s[sb]);
+    }
+  }
+  // s[sb][r] is the raw score of key j0 + 32 sb + 8 (r/4) + 4 hh + r%4.
+
+  if (TAIL) {  // keys >= N: neutral for the row extreme
+    const float neutral = c2 >= 0.f ? -INFINITY : INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N) s[sb][r] = neutral;
+  }
+
+  // Running max of the log2-scaled scores t = s * c2 (for c2 < 0 the max of
+  // t comes from the min of s).
+  float mt;
+  if (c2 >= 0.f) {
+    mt = xhalf_max(fmaxf(frag_max(s[0]), frag_max(s[1])));
+  } else {
+    mt = xhalf_min(fminf(frag_min(s[0]), frag_min(s[1])));
+  }
+  const float m_new = fmaxf(m, mt * c2);
+  const float alpha = fast_exp2(m - m_new);  // m = -inf on the first tile -> 0
+  m = m_new;
+
+  float rs = 0.f;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(fmaf(s[sb][r], c2, -m_new));
+      if (TAIL && (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N)) p = 0.f;
+      s[sb][r] = p;
+      rs += p;
+    }
+  l = l * alpha + rs;  // partial sum over this lane half's keys
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
+
+  // O^T += V^T P^T, 16 keys per MFMA.
+  const int p16 = lane & 15;
+  const int colhalf = (lane >> 4) & 1;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      const int b0 = 8 * hq;
+      const u32x4 pb = (u32x4){E::pack2(s[sb][b0 + 0], s[sb][b0 + 1]),
+                               E::pack2(s[sb][b0 + 2], s[sb][b0 + 3]),
+                               E::pack2(s[sb][b0 + 4], s[sb][b0 + 5]),
+                               E::pack2(s[sb][b0 + 6], s[sb][b0 + 7])};
+      // Transposing reads: lane (p16, group) points at row key0 + p16/4,
+      // columns c0 + 4*(p16%4) .. +3; it receives column c0 + p16 of rows
+      // key0 .. key0+3.
+      const int r0 = 32 * sb + 16 * hq + 4 * hh + (p16 >> 2);
+      const int r1 = r0 + 8;
+      const int half8 = (p16 & 1) * 8;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db) {
+        const int chunk = 4 * db + 2 * colhalf + ((p16 & 3) >> 1);
+        const unsigned char* a0 = vb + r0 * G::ROWB + ((chunk ^ swz_v<D>(r0)) << 4) + half8;
+        const unsigned char* a1 = vb + r1 * G::ROWB + ((chunk ^ swz_v<D>(r1)) << 4) + half8;
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1)));
+        const u32x4 a = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        acc[db] = E::mfma(a, pb, acc[db]);
+      }
+    }
+  }
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(kThreads) void attn_fwd_mfma16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int N, int nqt, float c2) {
+  using G = Geo16<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hh = lane >> 5;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / nqt, qt = tile - bh * nqt;
+  const size_t hoff = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + hoff;
+  const uint16_t* Kh = K + hoff;
+  const uint16_t* Vh = V + hoff;
+
+  // Q fragment, resident for the whole key loop: lane (li, hh) holds
+  // d = 16 ks + 8 hh + [0, 8) of query row qrow.
+  const int qrow = qt * G::BM + wave * 32 + li;
+  u32x4 qf[G::KS];
+  if (qrow < N) {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 8 * hh);
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) qf[ks] = qp[2 * ks];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) qf[ks] = (u32x4){0u, 0u, 0u, 0u};
+  }
+
+  f32x16 acc[G::DB];
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
+  float m = -INFINITY, l = 0.f;
+
+  const int ntiles = (N + G::BN - 1) / G::BN;
+  u32x4 kr[G::CPT], vr[G::CPT];
+  load_kv_regs<D>(Kh, Vh, 0, N, kr, vr);
+  store_kv_lds<D>(smem, smem + G::TILEB, kr, vr);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * G::BN;
+    const bool more = t + 1 < ntiles;
+    if (more) load_kv_regs<D>(Kh, Vh, j0 + G::BN, N, kr, vr);  // in flight during compute
+    const unsigned char* kb = smem + (t & 1) * 2 * G::TILEB;
+    const unsigned char* vb = kb + G::TILEB;
+    if (j0 + G::BN <= N)
+      tile_step16<E, D, false>(kb, vb, qf, acc, m, l, j0, N, c2);
+    else
+      tile_step16<E, D, true>(kb, vb, qf, acc, m, l, j0, N, c2);
+    if (more) {
+      unsigned char* nb = smem + ((t + 1) & 1) * 2 * G::TILEB;
+      store_kv_lds<D>(nb, nb + G::TILEB, kr, vr);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.
+  const float lt = xhalf_sum(l);
+  const float inv = 1.0f / lt;
+  if (qrow < N) {
+    uint16_t* op = O + hoff + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * hh;
+        const u32x2 w = (u32x2){E::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                                E::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + col) = w;
+      }
+    if (LSE != nullptr && hh == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: same structure on v_mfma_f32_32x32x2_f32, P kept in fp32.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Geo32 {
+  static constexpr int BM = 128;
+  static constexpr int BN = 32;
+  static constexpr int ROWB = D * 4;
+  static constexpr int CH = D / 4;             // 16-byte chunks per row
+  static constexpr int TILEB = BN * ROWB;
+  static constexpr int CPT = BN * CH / kThreads;
+  static constexpr int QV = D / 2;             // Q values per lane
+  static constexpr int DB = D / 32;
+  static constexpr int SMEM = 4 * TILEB;
+};
+
+// K rows are read 16 bytes at a time by 32 lanes of distinct rows; V rows are
+// read 128 contiguous bytes per lane half, the two halves 4 rows apart.
+template <int D> __device__ __forceinline__ int swz32_k(int row) { return row & 15; }
+template <int D> __device__ __forceinline__ int swz32_v(int row) { return ((row >> 2) & 1) << 3; }
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c2) {
+  using G = Geo32<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hh = lane >> 5;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / nqt, qt = tile - bh * nqt;
+  const size_t hoff = (size_t)bh * N * D;
+  const float* Qh = Q + hoff;
+  const float* Kh = K + hoff;
+  const float* Vh = V + hoff;
+
+  // Contraction index of K*Q^T: lane half hh covers d in [hh*D/2, (hh+1)*D/2),
+  // one d per MFMA k-step.
+  const int qrow = qt * G::BM + wave * 32 + li;
+  float qf[G::QV];
+  if (qrow < N) {
+    const f32x4* qp = reinterpret_cast<const f32x4*>(Qh + (size_t)qrow * D + hh * G::QV);
+#pragma unroll
+    for (int u = 0; u < G::QV / 4; ++u) {
+      const f32x4 x = qp[u];
+      qf[4 * u + 0] = x[0]; qf[4 * u + 1] = x[1]; qf[4 * u + 2] = x[2]; qf[4 * u + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < G::QV; ++u) qf[u] = 0.f;
+  }
+
+  f32x16 acc[G::DB];
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
+  float m = -INFINITY, l = 0.f;
+
+  const int ntiles = (N + G::BN - 1) / G::BN;
+  f32x4 kr[G::CPT], vr[G::CPT];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < G::CPT; ++u) {
+      const int ci = threadIdx.x + u * kThreads;
+      const int row = ci / G::CH, c = ci % G::CH;
+      if (j0 + row < N) {
+        const size_t off = (size_t)(j0 + row) * D + c * 4;
+        kr[u] = *reinterpret_cast<const f32x4*>(Kh + off);
+        vr[u] = *reinterpret_cast<const f32x4*>(Vh + off);
+      } else {
+        kr[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        vr[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto swrite = [&](unsigned char* kb, unsigned char* vb) {
+#pragma unroll
+    for (int u = 0; u < G::CPT; ++u) {
+      const int ci = threadIdx.x + u * kThreads;
+      const int row = ci / G::CH, c = ci % G::CH;
+      *reinterpret_cast<f32x4*>(kb + row * G::ROWB + ((c ^ swz32_k<D>(row)) << 4)) = kr[u];
+      *reinterpret_cast<f32x4*>(vb + row * G::ROWB + ((c ^ swz32_v<D>(row)) << 4)) = vr[u];
+    }
+  };
+  gload(0);
+  swrite(smem, smem + G::TILEB);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * G::BN;
+    const bool more = t + 1 < ntiles;
+    if (more) gload(j0 + G::BN);
+    const unsigned char* kb = smem + (t & 1) * 2 * G::TILEB;
+    const unsigned char* vb = kb + G::TILEB;
+
+    // S^T = K Q^T for 32 keys.
+    f32x16 s = (f32x16){};
+    {
+      const int row = li;
+      const unsigned char* rp = kb + row * G::ROWB;
+      const int sw = swz32_k<D>(row);
+#pragma unroll
+      for (int u = 0; u < G::QV / 4; ++u) {
+        const int c = hh * (G::QV / 4) + u;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(rp + ((c ^ sw) << 4));
+        s = mfma_f32(a[0], qf[4 * u + 0], s);
+        s = mfma_f32(a[1], qf[4 * u + 1], s);
+        s = mfma_f32(a[2], qf[4 * u + 2], s);
+        s = mfma_f32(a[3], qf[4 * u + 3], s);
+      }
+    }
+    const bool tail = j0 + G::BN > N;
+    if (tail) {
+      const float neutral = c2 >= 0.f ? -INFINITY : INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (j0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= N) s[r] = neutral;
+    }
+    const float mt = c2 >= 0.f ? xhalf_max(frag_max(s)) : xhalf_min(frag_min(s));
+    const float m_new = fmaxf(m, mt * c2);
+    const float alpha = fast_exp2(m - m_new);
+    m = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(fmaf(s[r], c2, -m_new));
+      if (tail && (j0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= N)) p = 0.f;
+      s[r] = p;
+      rs += p;
+    }
+    l = l * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
+
+    // O^T += V^T P^T: k-step r pairs P of key kr(hh) = 8(r/4) + 4hh + r%4
+    // (B, lane half hh) with V row kr(hh), column 32 db + li (A).
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const float* vrow = reinterpret_cast<const float*>(vb + row * G::ROWB);
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db) {
+        const int col = 32 * db + li;
+        const int c = col >> 2;
+        const float a = vrow[((c ^ swz32_v<D>(row)) << 2) + (col & 3)];
+        acc[db] = mfma_f32(a, s[r], acc[db]);
+      }
+    }
+    if (more) {
+      unsigned char* nb = smem + ((t + 1) & 1) * 2 * G::TILEB;
+      swrite(nb, nb + G::TILEB);
+    }
+    __syncthreads();
+  }
+
+  const float lt = xhalf_sum(l);
+  const float inv = 1.0f / lt;
+  if (qrow < N) {
+    float* op = O + hoff + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * hh;
+        *reinterpret_cast<f32x4*>(op + col) =
+            (f32x4){acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv,
+                    acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+      }
+    if (LSE != nullptr && hh == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+template <class T>
+int launch(void (*kernel)(const T*, const T*, const T*, T*, float*, int, int, float),
+           int64_t nblocks, hipStream_t stream, const void* q, const void* k, const void* v,
+           void* o, float* lse, int N, int nqt, float c2) {
+  hipLaunchKernelGGL(kernel, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(k),
+                     static_cast<const T*>(v), static_cast<T*>(o), lse, N, nqt, c2);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype,
+                        void* stream) {
+  // --- validation: no HIP call before this block has passed -------------
+  if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16)
+    return ATTN_ERR_DTYPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  int64_t bh = 0, bhn = 0, elems = 0;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &elems))
+    return ATTN_ERR_SHAPE;
+  if (bhn == 0) return ATTN_OK;  // empty: nothing to launch
+  if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULLPTR;
+  const size_t esize = dtype == ATTN_DTYPE_F32 ? 4 : 2;
+  if (elems > INT64_MAX / (int64_t)esize) return ATTN_ERR_SHAPE;
+  const int64_t nqt = (N + 127) / 128;  // BM = 128 for every instance
+  int64_t nblocks = 0;
+  if (!mul_ok(bh, nqt, &nblocks) || nblocks > INT32_MAX) return ATTN_ERR_SHAPE;
+  auto misaligned = [](const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+  };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+      (lse != nullptr && misaligned(lse, 4)))
+    return ATTN_ERR_ALIGN;
+  const size_t tbytes = (size_t)elems * esize, lbytes = (size_t)bhn * 4;
+  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
+      overlaps(o, tbytes, v, tbytes))
+    return ATTN_ERR_ALIAS;
+  if (lse != nullptr && (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) ||
+                         overlaps(lse, lbytes, v, tbytes) || overlaps(lse, lbytes, o, tbytes)))
+    return ATTN_ERR_ALIAS;
+
+  // --- launch -------------------------------------------------------------
+  const float c2 = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int n = (int)N, nq = (int)nqt;
+  if (dtype == ATTN_DTYPE_BF16) {
+    if (d == 128) return launch(attn_fwd_mfma16<Bf16T, 128>, nblocks, s, q, k, v, o, lse, n, nq, c2);
+    return launch(attn_fwd_mfma16<Bf16T, 64>, nblocks, s, q, k, v, o, lse, n, nq, c2);
+  }
+  if (dtype == ATTN_DTYPE_F16) {
+    if (d == 128) return launch(attn_fwd_mfma16<F16T, 128>, nblocks, s, q, k, v, o, lse, n, nq, c2);
+    return launch(attn_fwd_mfma16<F16T, 64>, nblocks, s, q, k, v, o, lse, n, nq, c2);
+  }
+  if (d == 128) return launch(attn_fwd_mfma32<128>, nblocks, s, q, k, v, o, lse, n, nq, c2);
+  return launch(attn_fwd_mfma32<64>, nblocks, s, q, k, v, o, lse, n, nq, c2);
+}
+
+extern "C" const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULLPTR: return "q, k, v or o is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape: negative size, overflow, N > ATTN_MAX_N or grid too large";
+    case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (need 64 or 128)";
+    case ATTN_ERR_DTYPE: return "unknown dtype";
+    case ATTN_ERR_SCALE: return "scale is not finite";
+    case ATTN_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
+    case ATTN_ERR_ALIAS: return "an output overlaps an input (or lse overlaps o)";
+    case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int attn_version(void) { return 100; }

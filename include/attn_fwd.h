@@ -1,0 +1,94 @@
+/*
+ * attn_fwd.h - C ABI of the MI355X (gfx950) fused attention forward.
+ *
+ * The operation (page 3 "OpenAI Triton from introduction to model practice",
+ * section 5, the FlashAttention forward kernel that stores the output and the
+ * log-sum-exp; section 3 for the plain definition it replaces):
+ *
+ *   for every batch b < B, head h < H and query row i < N:
+ *     s_ij        = scale * sum_c Q[b,h,i,c] * K[b,h,j,c]          (j < N)
+ *     O[b,h,i,:]  = sum_j softmax_j(s_i.) * V[b,h,j,:]
+ *     lse[b,h,i]  = ln sum_j exp(s_ij)      (natural log, scaled scores)
+ *
+ * computed tile by tile with an online softmax (page 1 "Triton hand-written
+ * kernels", section 4: running row max m, running exp-sum l, rescaled fp32
+ * accumulator), so the N x N score matrix never reaches device memory.
+ * Self-attention (queries and keys share N), non-causal.
+ *
+ * Everything here is plain C: pointers, sizes and an opaque stream handle.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O.  lse is always fp32. */
+typedef enum {
+  ATTN_DTYPE_F32 = 0,  /* IEEE binary32; QK^T and PV on fp32 MFMA, P kept fp32  */
+  ATTN_DTYPE_F16 = 1,  /* IEEE binary16; fp16 MFMA, fp32 accumulate, P -> fp16  */
+  ATTN_DTYPE_BF16 = 2  /* bfloat16;      bf16 MFMA, fp32 accumulate, P -> bf16  */
+} attn_dtype_t;
+
+/* Return codes.  Every error is detected before any HIP call is made, except
+ * ATTN_ERR_HIP; on any error nothing is launched and no output is written. */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULLPTR = -1,  /* q, k, v or o is NULL while B*H*N > 0              */
+  ATTN_ERR_SHAPE = -2,    /* a size is negative, or B*H*N*d overflows int64,
+                             or N exceeds ATTN_MAX_N, or the grid is too large */
+  ATTN_ERR_HEAD_DIM = -3, /* d is not 64 or 128                                 */
+  ATTN_ERR_DTYPE = -4,    /* dtype is not an attn_dtype_t value                 */
+  ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite                           */
+  ATTN_ERR_ALIGN = -6,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte  */
+  ATTN_ERR_ALIAS = -7,    /* o or lse overlaps an input, or lse overlaps o      */
+  ATTN_ERR_HIP = -8       /* the kernel launch failed (hipGetLastError)         */
+};
+
+/* Largest sequence length accepted: per-head offsets are 32-bit in-kernel. */
+#define ATTN_MAX_N (1 << 24)
+
+/*
+ * attn_fwd - O = softmax(scale * Q K^T) V and lse, for all B*H heads.
+ *
+ * q, k, v : device pointers, [B, H, N, d] contiguous (row-major, d fastest),
+ *           element type `dtype`.  Read only.
+ * o       : device pointer, [B, H, N, d] contiguous, element type `dtype`.
+ *           Written: O rounded to nearest-even from the fp32 accumulator.
+ * lse     : device pointer, [B, H, N] fp32, or NULL to skip it.  Written:
+ *           m + ln l of the scaled scores.
+ * B, H, N : batch, heads, sequence length (queries = keys = N).  Any >= 0;
+ *           N need not be a multiple of any tile size (tails are masked:
+ *           padded keys get probability 0, padded query rows are not stored).
+ * d       : head dimension, 64 or 128.
+ * scale   : multiplies Q K^T before the softmax; any finite value (the usual
+ *           choice is 1/sqrt(d)).
+ * dtype   : an attn_dtype_t value.
+ * stream  : a hipStream_t (NULL = the null stream).  The launch is
+ *           asynchronous and ordered on this stream; the call never
+ *           synchronises, allocates or frees anything, and keeps no state.
+ *
+ * Ownership: the caller owns every buffer and must keep them alive until the
+ * stream work completes.  Pointers must be device memory of the current
+ * device (not checked: host pointers fault).  Outputs must not overlap inputs.
+ * B*H*N == 0 returns ATTN_OK without launching anything.
+ * Results are deterministic: the same inputs give bit-identical outputs.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype,
+             void* stream);
+
+/* Static text for a return code (never NULL). */
+const char* attn_strerror(int code);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,99 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments before making any HIP call."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from attention_attn_fwd_07_amd import build as build_mod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULLPTR, SHAPE, HEAD_DIM, DTYPE, SCALE, ALIGN, ALIAS, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+F32, F16, BF16 = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = build_mod.ensure_built()
+    l = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    l.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                           ctypes.c_int, vp]
+    l.attn_fwd.restype = ctypes.c_int
+    l.attn_strerror.argtypes = [ctypes.c_int]
+    l.attn_strerror.restype = ctypes.c_char_p
+    return l
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \t\*]*?\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text,
+                            flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    assert {"attn_fwd", "attn_strerror", "attn_version"} <= set(declared_functions())
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+
+
+def test_version_and_strerror(lib):
+    lib.attn_version.restype = ctypes.c_int
+    assert lib.attn_version() >= 100
+    for code in (OK, NULLPTR, SHAPE, HEAD_DIM, DTYPE, SCALE, ALIGN, ALIAS, HIP, 12345):
+        assert lib.attn_strerror(code)
+
+
+# distinct, 16-byte aligned fake device addresses; validation never touches them
+Q, K, V, O, L = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+
+def call(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=128, d=64, scale=0.125, dtype=BF16):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), SHAPE), (dict(H=-3), SHAPE), (dict(N=-1), SHAPE), (dict(d=-64), SHAPE),
+    (dict(dtype=3), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(d=32), HEAD_DIM), (dict(d=96), HEAD_DIM), (dict(d=256), HEAD_DIM), (dict(d=0), HEAD_DIM),
+    (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE),
+    (dict(scale=float("-inf")), SCALE),
+    (dict(q=None), NULLPTR), (dict(k=None), NULLPTR), (dict(v=None), NULLPTR),
+    (dict(o=None), NULLPTR),
+    (dict(q=Q + 8), ALIGN), (dict(o=O + 2), ALIGN), (dict(v=V + 4), ALIGN), (dict(lse=L + 2), ALIGN),
+    (dict(o=Q), ALIAS), (dict(o=K + 64), ALIAS), (dict(lse=V), ALIAS), (dict(lse=O + 16), ALIAS),
+    (dict(N=(1 << 24) + 1), SHAPE),
+    (dict(B=1 << 40, H=1 << 30), SHAPE),
+])
+def test_rejects_before_any_hip_call(lib, kw, code):
+    assert call(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=None, o=None),
+                                dict(B=0, d=128, dtype=F32)])
+def test_empty_is_a_no_op(lib, kw):
+    assert call(lib, **kw) == OK
+
+
+def test_shape_checked_before_emptiness(lib):
+    # bad head dim or dtype is an error even for empty input
+    assert call(lib, N=0, d=80) == HEAD_DIM
+    assert call(lib, N=0, dtype=7) == DTYPE
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import attention_attn_fwd_07_amd as attn
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attn_fwd(q, q, q, torch.empty_like(q), None, 0.125)

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP attention forward against the fp64 oracle.
+
+Inputs come from ``datagen`` (seeded, rounded to the dtype on the CPU); both
+sides read the same rounded values.  Bars (element by element, whole tensor):
+
+* fp32 inputs:        max |O - O_ref| <= 1e-4
+* bf16 / fp16 inputs: max |O - O_ref| <= 2e-2 and
+                      ||O - O_ref||_F / ||O_ref||_F <= 5e-3
+* lse (fp32 output):  max |lse - lse_ref| <= 1e-4 (fp32 inputs), 1e-3 (16-bit)
+
+The long workloads (N = 16384 and 65536) are compared on sampled query rows
+(every head, tile edges, random rows, and the rows with the largest |O|),
+which the oracle computes exactly row by row, plus properties that hold at any
+size on the whole output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(maxabs=1e-4, relf=None, lse=1e-4),
+       "f16": dict(maxabs=2e-2, relf=5e-3, lse=1e-3),
+       "bf16": dict(maxabs=2e-2, relf=5e-3, lse=1e-3)}
+
+
+def _attn():
+    import attention_attn_fwd_07_amd as attn
+    return attn
+
+
+def run_gpu(q, k, v, scale, with_lse=True, stream=None):
+    attn = _attn()
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev) if with_lse else None
+    attn.attn_fwd(qd, kd, vd, o, lse, scale, stream=stream)
+    torch.cuda.synchronize()
+    o64 = o.cpu().double().numpy()
+    lse64 = lse.cpu().double().numpy() if with_lse else None
+    return o64, lse64
+
+
+def check(o, lse, o_ref, lse_ref, dtype, what=""):
+    tol = TOL[dtype]
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    err = np.abs(o - o_ref)
+    maxabs = float(err.max()) if err.size else 0.0
+    assert maxabs <= tol["maxabs"], f"{what}: max-abs {maxabs:.3e} > {tol['maxabs']}"
+    if tol["relf"] is not None and o_ref.size:
+        relf = float(np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref))
+        assert relf <= tol["relf"], f"{what}: rel-Frobenius {relf:.3e} > {tol['relf']}"
+    if lse is not None and lse_ref.size:
+        lerr = float(np.abs(lse - lse_ref).max())
+        assert lerr <= tol["lse"], f"{what}: lse max-abs {lerr:.3e} > {tol['lse']}"
+
+
+def full_parity(q, k, v, scale, dtype, what):
+    o, lse = run_gpu(q, k, v, scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale)
+    check(o, lse, o_ref, lse_ref, dtype, what)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("key", [1, 2, 3])
+def test_workload_full_parity(key):
+    w = datagen.WORKLOADS[key]
+    q, k, v = datagen.workload_inputs(key)
+    full_parity(q, k, v, w.scale, w.dtype, w.name)
+
+
+def _sample_index(o_gpu, B, H, N, rng, per_head=24, top=64):
+    rows = set()
+    for b in range(B):
+        for h in range(H):
+            for i in (0, 1, 127, 128, N // 2, N - 2, N - 1):
+                rows.add((b, h, i))
+            for i in rng.choice(N, size=per_head, replace=False):
+                rows.add((b, h, int(i)))
+    mag = np.abs(o_gpu).max(axis=-1).reshape(-1)
+    for flat in np.argpartition(mag, -top)[-top:]:
+        b, rem = divmod(int(flat), H * N)
+        h, i = divmod(rem, N)
+        rows.add((b, h, i))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("key", [4, 5])
+def test_workload_sampled_parity(key):
+    w = datagen.WORKLOADS[key]
+    q, k, v = datagen.workload_inputs(key)
+    o, lse = run_gpu(q, k, v, w.scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(1000 + key)
+    idx = _sample_index(o, w.B, w.H, w.N, rng)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, w.scale, idx)
+    b, h, i = idx[:, 0], idx[:, 1], idx[:, 2]
+    check(o[b, h, i], lse[b, h, i], o_ref, lse_ref, w.dtype, f"{w.name} ({len(idx)} rows)")
+    # whole-tensor property: every output lies in the convex hull of V's rows
+    v64 = v.double().numpy()
+    lo = v64.min(axis=2, keepdims=True) - TOL[w.dtype]["maxabs"]
+    hi = v64.max(axis=2, keepdims=True) + TOL[w.dtype]["maxabs"]
+    assert np.all(o >= lo) and np.all(o <= hi)
+
+
+# ---------------------------------------------------------------------------
+# ragged and small shapes, every dtype and head dim
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 17, 63, 64, 65, 127, 129, 257, 1000])
+def test_ragged_shapes(dtype, d, N):
+    q, k, v = datagen.make_qkv(2, 3, N, d, dtype, seed=N * 7 + d)
+    full_parity(q, k, v, 1.0 / math.sqrt(d), dtype, f"{dtype} d={d} N={N}")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_seeds_multi_tile(seed):
+    q, k, v = datagen.make_qkv(1, 4, 777, 128, "bf16", seed=seed)
+    full_parity(q, k, v, 1.0 / math.sqrt(128), "bf16", f"seed {seed}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_hot_keys_rescaling(dtype):
+    q, k, v = datagen.make_qkv(1, 2, 3000, 64, dtype, seed=55, hot_frac=0.01, hot_mult=8.0)
+    full_parity(q, k, v, 0.125, dtype, f"hot keys {dtype}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 2.0])
+def test_scales(scale):
+    q, k, v = datagen.make_qkv(1, 2, 300, 64, "f32", seed=77)
+    full_parity(q, k, v, scale, "f32", f"scale {scale}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_scores_do_not_overflow(dtype):
+    """Scores of order 1e3 (exp without max subtraction would overflow).
+
+    The fp32 score itself then carries an absolute rounding error of order
+    1e-7 * sum_c |q_c k_c| ~ 1e-4, which moves softmax weights by that relative
+    amount, so fp32 O is held to 5e-3 here and lse to 1e-6 relative.  bf16 O is
+    also rounded to bf16 on output (half an ulp is 2^-8 |O|, 7.8e-3 at |O| ~ 2),
+    so it is held to the 16-bit bar of 2e-2.
+    """
+    q, k, v = datagen.make_qkv(1, 2, 200, 64, dtype, seed=78)
+    q = q * 64.0  # exact: a power of two
+    o, lse = run_gpu(q, k, v, 1.0)
+    o_ref, lse_ref = oracle.attention(q, k, v, 1.0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.abs(lse_ref).max() > 300.0
+    assert np.abs(o - o_ref).max() <= (5e-3 if dtype == "f32" else TOL[dtype]["maxabs"])
+    assert np.all(np.abs(lse - lse_ref) <= 1e-6 * np.abs(lse_ref) + 1e-4)
+
+
+# ---------------------------------------------------------------------------
+# behaviour
+# ---------------------------------------------------------------------------
+
+def test_deterministic_bitwise():
+    q, k, v = datagen.make_qkv(2, 4, 1000, 128, "bf16", seed=9)
+    attn = _attn()
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    outs = []
+    for _ in range(3):
+        o, lse = attn.fwd(qd, kd, vd)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).cpu(), lse.cpu()))
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+
+
+def test_without_lse_same_output():
+    q, k, v = datagen.make_qkv(1, 2, 300, 64, "bf16", seed=10)
+    o1, _ = run_gpu(q, k, v, 0.125, with_lse=True)
+    o2, _ = run_gpu(q, k, v, 0.125, with_lse=False)
+    assert np.array_equal(o1, o2)
+
+
+def test_side_stream():
+    q, k, v = datagen.make_qkv(1, 2, 300, 128, "f16", seed=11)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = run_gpu(q, k, v, 0.1, stream=s)
+    o_ref, lse_ref = oracle.attention(q, k, v, 0.1)
+    check(o, lse, o_ref, lse_ref, "f16", "side stream")
+
+
+def test_empty_sequence_is_a_no_op():
+    attn = _attn()
+    q = torch.zeros(2, 3, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = attn.fwd(q, q, q)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 64) and lse.shape == (2, 3, 0)
+
+
+def test_nan_key_poisons_its_head_only():
+    q, k, v = datagen.make_qkv(1, 2, 200, 64, "bf16", seed=12)
+    k[0, 0, 150, 3] = float("nan")
+    o, lse = run_gpu(q, k, v, 0.125)
+    assert np.all(np.isnan(o[0, 0])) and np.all(np.isnan(lse[0, 0]))
+    assert np.all(np.isfinite(o[0, 1])) and np.all(np.isfinite(lse[0, 1]))
+
+
+def test_binding_rejects_bad_arguments():
+    attn = _attn()
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        attn.fwd(q, q, q.float())
+    q32 = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        attn.fwd(q32, q32, q32)  # d = 32 unsupported
+    with pytest.raises(ValueError):
+        attn.fwd(q.transpose(2, 3), q.transpose(2, 3), q.transpose(2, 3))
+    with pytest.raises(ValueError):
+        attn.attn_fwd(q, q, q, q, None, 0.125)  # output aliases an input

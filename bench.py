@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark the MI355X attention forward; prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+A step is one ``attn_fwd`` call over the whole workload (every step of the
+fused forward: Q tile load, K/V streaming, QK^T, online softmax, PV, O and
+lse stores), on inputs already resident in device memory.  The default
+workload is B=2, H=16, N=4096, d=128 bf16 (the 4096-length case whose
+4096x4096 score matrix must never be materialised); ``--workload`` selects any
+of the five synthetic workloads.
+
+Timing: W untimed warmup launches, then exactly K launches back to back on
+torch's current stream, bracketed by torch.cuda.synchronize() on both sides
+(wall clock for ms_per_step) and by HIP events recorded on that same stream
+between consecutive launches (per-launch kernel durations for the roofline).
+
+Roofline: flops = 4*B*H*N^2*d per launch against the dense bf16/fp16 MFMA
+peak of 2500 TFLOP/s (fp32 workloads: 157.3 TFLOP/s fp32 matrix peak).
+``traffic`` is read from profiles/traffic.json (rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters, calibrated against a plain copy) and reported only while
+the kernel source is unchanged since those counters were taken.
+
+cpu_baseline: the fp64 CPU oracle, as it stands, timed on this host's cores on
+a bounded sample of the same workload (whole heads until ~10 s have passed).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of MI355X bf16 MFMA peak"
+KERNEL_SRC = os.path.join(ROOT, "attention_attn_fwd_07_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> int:
+    """Q, K, V read once, O written once, lse written once."""
+    return 4 * w.B * w.H * w.N * w.d * w.elem_bytes + 4 * w.B * w.H * w.N
+
+
+def traffic_for(w):
+    """Measured HBM bytes per launch, if counters exist for this exact kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(str(w.key))
+    if not entry or rec.get("kernel_sha256_16") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s: float = 10.0):
+    """Time the oracle on a bounded sample of the workload.
+
+    Units of work are whole heads (N <= 8192) or 512-query-row slices of a head
+    (longer sequences), each against all N keys, taken in order until the
+    budget is used.  The rate is scaled to the metric's unit (TFLOP/s of the
+    4*rows*N*d algorithmic flops the sample covers).
+    """
+    import numpy as np
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    q64, k64, v64 = (t.double().numpy() for t in (q, k, v))
+    rows_per_unit = w.N if w.N <= 8192 else 512
+    done, t0 = 0, time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            for r0 in range(0, w.N, rows_per_unit):
+                rows = np.arange(r0, min(w.N, r0 + rows_per_unit))
+                idx = np.stack([np.full(len(rows), b), np.full(len(rows), h), rows], axis=1)
+                oracle.attention_rows(q64, k64, v64, w.scale, idx, workers=cores)
+                done += len(rows)
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            else:
+                continue
+            break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    total = w.B * w.H * w.N
+    return {"value": round(4.0 * done * w.N * w.d / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {total} query rows (units of {rows_per_unit} rows of one head),"
+                      f" each against all {w.N} keys; fp64 numpy on {cores} threads; {dt:.1f} s",
+            "full_workload_seconds_extrapolated": round(dt * total / done, 1)}
+
+
+def calibrate_copy(nbytes: int, reps: int) -> None:
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}))
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this attention forward runs on one GPU; multi-GPU runs are not "
+              "part of this build (heads or batches would shard with no communication).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return 0
+
+    import attention_attn_fwd_07_amd as attn
+    import datagen
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU available", file=sys.stderr)
+        return 1
+    w = datagen.WORKLOADS[args.workload]
+    q, k, v = datagen.workload_inputs(w.key)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        attn.attn_fwd(qd, kd, vd, o, lse, w.scale)
+    K = args.steps
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    events[0].record(stream)
+    for i in range(K):
+        attn.attn_fwd(qd, kd, vd, o, lse, w.scale)
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = sorted(events[i].elapsed_time(events[i + 1]) for i in range(K))  # ms
+    kern_ms = events[0].elapsed_time(events[K]) / K
+    ms_per_step = wall * 1e3 / K
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    def q_(p):
+        return per[min(K - 1, int(round(p * (K - 1))))]
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": w.describe(),
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "kernel_ms": {"mean": round(kern_ms, 5), "p20": round(q_(0.2), 5),
+                      "median": round(q_(0.5), 5), "p80": round(q_(0.8), 5)},
+        "hbm_gbps_algorithmic": round(algorithmic_bytes(w) / (kern_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_for(w)},
+        "kernel_sha256_16": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -143,14 +143,16 @@ struct Geo16 {
   static constexpr int ROWB = D * 2;           // bytes per K/V row
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int TILEB = BN * ROWB;      // bytes of one K or V tile
-  static constexpr int CPT = BN * CH / kThreads;  // chunks each thread moves
   static constexpr int KS = D / 16;            // k-steps of K*Q^T
   static constexpr int DB = D / 32;            // 32-wide column blocks of O
   static constexpr int SMEM = 4 * TILEB;       // K,V x 2 buffers
+  static constexpr int LOADB = 64 * 16;        // bytes one wave-wide 16-byte load moves
+  static constexpr int ROWS_PER_LOAD = LOADB / ROWB;
+  static constexpr int LOADS_PER_WAVE = TILEB / LOADB / (kThreads / 64);
 };
 
 // LDS swizzles: physical 16-byte chunk = logical chunk ^ f(row).
-//  K is read as 16-byte rows fragments by 32 lanes of distinct rows: XOR the
+//  K is read as 16-byte row fragments by 32 lanes of distinct rows: XOR the
 //  chunk with the row so that consecutive rows hit distinct banks.
 //  V is read by ds_read_b64_tr_b16 as 8 rows x 64 bytes per wave: XOR bits 2-3
 //  of the chunk so that the 8 rows spread over the whole bank range.
@@ -161,40 +163,86 @@ template <int D> __device__ __forceinline__ int swz_v(int row);
 template <> __device__ __forceinline__ int swz_v<128>(int row) { return (row & 3) << 2; }
 template <> __device__ __forceinline__ int swz_v<64>(int row) { return ((row >> 1) & 1) << 2; }
 
+typedef __attribute__((address_space(1))) void gmem_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Stream one K tile and one V tile (keys j0 .. j0+63) straight from global
+// memory into LDS with 16-byte direct loads (global_load_lds_dwordx4): lane i
+// of a wave-wide load fills bytes [16 i, 16 i + 16) of a 1 KiB LDS block, so
+// the swizzle is applied on the source side, by choosing which chunk each
+// lane fetches.  Every row of a tile is a contiguous 2*d-byte run of K or V,
+// read whole by CH consecutive lanes (coalesced).
+//
+// Load u of wave w fills block u*4 + w, i.e. rows 16u + r0 (d = 128) or
+// 32u + r0 (d = 64) with r0 = w * ROWS_PER_LOAD + lane / CH.  The swizzle
+// bits of those rows do not depend on u, so each lane's byte offset within
+// the 16/32-row group is a loop invariant and the per-load base is uniform.
 template <int D>
-__device__ __forceinline__ void load_kv_regs(const uint16_t* __restrict__ Kh,
-                                             const uint16_t* __restrict__ Vh, int j0, int N,
-                                             u32x4 (&kr)[Geo16<D>::CPT],
-                                             u32x4 (&vr)[Geo16<D>::CPT]) {
+struct TileLoader {
   using G = Geo16<D>;
+  static constexpr int NW = kThreads / 64;
+  static constexpr int STEP_ROWS = NW * G::ROWS_PER_LOAD;  // rows between loads u, u+1
+  static_assert(STEP_ROWS % 16 == 0, "swizzle bits must not depend on u");
+  uint32_t koff, voff;  // this lane's byte offset from the group's first row
+  int r0;               // this lane's row within a group
+
+  __device__ __forceinline__ TileLoader() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    r0 = wave * G::ROWS_PER_LOAD + lane / G::CH;
+    const int p = lane % G::CH;
+    koff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_k<D>(r0)) << 4));
+    voff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_v<D>(r0)) << 4));
+  }
+
+  // Full tile: rows j0 .. j0+63 all exist.
+  __device__ __forceinline__ void full(const unsigned char* Kb, const unsigned char* Vb, int j0,
+                                       unsigned char* kb, unsigned char* vb) const {
+    const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int u = 0; u < G::CPT; ++u) {
-    const int ci = threadIdx.x + u * kThreads;
-    const int row = ci / G::CH, c = ci % G::CH;
-    if (j0 + row < N) {
-      const size_t off = (size_t)(j0 + row) * D + c * 8;
-      kr[u] = *reinterpret_cast<const u32x4*>(Kh + off);
-      vr[u] = *reinterpret_cast<const u32x4*>(Vh + off);
-    } else {  // padded key rows: zeros, so P (=0) * V stays 0
-      kr[u] = (u32x4){0u, 0u, 0u, 0u};
-      vr[u] = (u32x4){0u, 0u, 0u, 0u};
+    for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
+      const size_t base = (size_t)(j0 + u * STEP_ROWS) * G::ROWB;
+      const int blk = u * NW + wave;
+      __builtin_amdgcn_global_load_lds((gmem_void*)(Kb + base + koff),
+                                       (lds_void*)(kb + blk * G::LOADB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gmem_void*)(Vb + base + voff),
+                                       (lds_void*)(vb + blk * G::LOADB), 16, 0, 0);
     }
   }
-}
 
-template <int D>
-__device__ __forceinline__ void store_kv_lds(unsigned char* kb, unsigned char* vb,
-                                             const u32x4 (&kr)[Geo16<D>::CPT],
-                                             const u32x4 (&vr)[Geo16<D>::CPT]) {
-  using G = Geo16<D>;
+  // Last, partial tile: rows past N-1 re-read row N-1 (in bounds); their
+  // scores are masked and their probabilities are zero.
+  __device__ __forceinline__ void tail(const unsigned char* Kb, const unsigned char* Vb, int j0,
+                                       int N, unsigned char* kb, unsigned char* vb) const {
+    const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int u = 0; u < G::CPT; ++u) {
-    const int ci = threadIdx.x + u * kThreads;
-    const int row = ci / G::CH, c = ci % G::CH;
-    *reinterpret_cast<u32x4*>(kb + row * G::ROWB + ((c ^ swz_k<D>(row)) << 4)) = kr[u];
-    *reinterpret_cast<u32x4*>(vb + row * G::ROWB + ((c ^ swz_v<D>(row)) << 4)) = vr[u];
+    for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
+      const int r = u * STEP_ROWS + r0;
+      const int grow = min(j0 + r, N - 1);
+      const size_t rowbase = (size_t)grow * G::ROWB;
+      const uint32_t kc = koff - (uint32_t)(r0 * G::ROWB), vc = voff - (uint32_t)(r0 * G::ROWB);
+      const int blk = u * NW + wave;
+      __builtin_amdgcn_global_load_lds((gmem_void*)(Kb + rowbase + kc),
+                                       (lds_void*)(kb + blk * G::LOADB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gmem_void*)(Vb + rowbase + vc),
+                                       (lds_void*)(vb + blk * G::LOADB), 16, 0, 0);
+    }
   }
-}
+
+  __device__ __forceinline__ void load(const unsigned char* Kb, const unsigned char* Vb, int j0,
+                                       int N, unsigned char* kb, unsigned char* vb) const {
+    if (j0 + G::BN <= N)
+      full(Kb, Vb, j0, kb, vb);
+    else
+      tail(Kb, Vb, j0, N, kb, vb);
+  }
+};
+
+// The reference max m (log2 domain) moves only when some row of the wave
+// exceeds it by more than this many doublings; until then P = 2^(t - m) may
+// reach 2^8, harmless in fp32 and in bf16/fp16 (same relative precision).
+// The result is the same softmax: O = acc / l with acc and l built from the
+// same reference.
+constexpr float kRescaleThreshold = 8.0f;
 
 // One K/V tile: scores, online-softmax update, P.V accumulate.
 template <class E, int D, bool TAIL>
@@ -231,31 +279,47 @@ __device__ __forceinline__ void tile_step16(const unsigned char* kb, const unsig
         if (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N) s[sb][r] = neutral;
   }
 
-  // Running max of the log2-scaled scores t = s * c2 (for c2 < 0 the max of
-  // t comes from the min of s).
+  // Tile max of the log2-scaled scores t = s * c2 (for c2 < 0 the max of t
+  // comes from the min of s).
   float mt;
   if (c2 >= 0.f) {
     mt = xhalf_max(fmaxf(frag_max(s[0]), frag_max(s[1])));
   } else {
     mt = xhalf_min(fminf(frag_min(s[0]), frag_min(s[1])));
   }
-  const float m_new = fmaxf(m, mt * c2);
-  const float alpha = fast_exp2(m - m_new);  // m = -inf on the first tile -> 0
-  m = m_new;
+  const float m_tile = mt * c2;
+  if (__builtin_amdgcn_ballot_w64(m_tile > m + kRescaleThreshold) != 0) {  // wave-uniform
+    const float m_new = fmaxf(m, m_tile);
+    const float alpha = fast_exp2(m - m_new);  // m = -inf on the first tile -> 0
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
+  }
 
+  // P = 2^(t - m); the row sum takes the fp32 values (the log-sum-exp output
+  // depends on it directly), the MFMA takes them rounded to the element type.
+  u32x4 pb[2][2];
   float rs = 0.f;
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+  for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(fmaf(s[sb][r], c2, -m_new));
+      float p = fast_exp2(fmaf(s[sb][r], c2, -m));
       if (TAIL && (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N)) p = 0.f;
       s[sb][r] = p;
       rs += p;
     }
-  l = l * alpha + rs;  // partial sum over this lane half's keys
 #pragma unroll
-  for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
+    for (int hq = 0; hq < 2; ++hq) {
+      const int b0 = 8 * hq;
+      pb[sb][hq] = (u32x4){E::pack2(s[sb][b0 + 0], s[sb][b0 + 1]),
+                           E::pack2(s[sb][b0 + 2], s[sb][b0 + 3]),
+                           E::pack2(s[sb][b0 + 4], s[sb][b0 + 5]),
+                           E::pack2(s[sb][b0 + 6], s[sb][b0 + 7])};
+    }
+  }
+  l += rs;
 
   // O^T += V^T P^T, 16 keys per MFMA.
   const int p16 = lane & 15;
@@ -264,11 +328,6 @@ __device__ __forceinline__ void tile_step16(const unsigned char* kb, const unsig
   for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
-      const int b0 = 8 * hq;
-      const u32x4 pb = (u32x4){E::pack2(s[sb][b0 + 0], s[sb][b0 + 1]),
-                               E::pack2(s[sb][b0 + 2], s[sb][b0 + 3]),
-                               E::pack2(s[sb][b0 + 4], s[sb][b0 + 5]),
-                               E::pack2(s[sb][b0 + 6], s[sb][b0 + 7])};
       // Transposing reads: lane (p16, group) points at row key0 + p16/4,
       // columns c0 + 4*(p16%4) .. +3; it receives column c0 + p16 of rows
       // key0 .. key0+3.
@@ -285,17 +344,17 @@ __device__ __forceinline__ void tile_step16(const unsigned char* kb, const unsig
         const u32x2 hi = __builtin_bit_cast(
             u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1)));
         const u32x4 a = (u32x4){lo[0], lo[1], hi[0], hi[1]};
-        acc[db] = E::mfma(a, pb, acc[db]);
+        acc[db] = E::mfma(a, pb[sb][hq], acc[db]);
       }
     }
   }
 }
 
 template <class E, int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_mfma16(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int N, int nqt, float c2) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                     float* __restrict__ LSE, int N, int nqt, float c2) {
   using G = Geo16<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM];
 
@@ -308,6 +367,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma16(
   const uint16_t* Qh = Q + hoff;
   const uint16_t* Kh = K + hoff;
   const uint16_t* Vh = V + hoff;
+
+  const int ntiles = (N + G::BN - 1) / G::BN;
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(Kh);
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(Vh);
+  const TileLoader<D> loader;
+  loader.load(Kb, Vb, 0, N, smem, smem + G::TILEB);
 
   // Q fragment, resident for the whole key loop: lane (li, hh) holds
   // d = 16 ks + 8 hh + [0, 8) of query row qrow.
@@ -327,27 +392,25 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma16(
   for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
   float m = -INFINITY, l = 0.f;
 
-  const int ntiles = (N + G::BN - 1) / G::BN;
-  u32x4 kr[G::CPT], vr[G::CPT];
-  load_kv_regs<D>(Kh, Vh, 0, N, kr, vr);
-  store_kv_lds<D>(smem, smem + G::TILEB, kr, vr);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Full tiles in the loop; the one partial tile (if N % 64 != 0) after it.
+  const int nfull = N / G::BN;
+  for (int t = 0; t < nfull; ++t) {
     const int j0 = t * G::BN;
-    const bool more = t + 1 < ntiles;
-    if (more) load_kv_regs<D>(Kh, Vh, j0 + G::BN, N, kr, vr);  // in flight during compute
-    const unsigned char* kb = smem + (t & 1) * 2 * G::TILEB;
-    const unsigned char* vb = kb + G::TILEB;
-    if (j0 + G::BN <= N)
-      tile_step16<E, D, false>(kb, vb, qf, acc, m, l, j0, N, c2);
-    else
-      tile_step16<E, D, true>(kb, vb, qf, acc, m, l, j0, N, c2);
-    if (more) {
-      unsigned char* nb = smem + ((t + 1) & 1) * 2 * G::TILEB;
-      store_kv_lds<D>(nb, nb + G::TILEB, kr, vr);
-    }
-    __syncthreads();
+    unsigned char* cur = smem + (t & 1) * 2 * G::TILEB;
+    unsigned char* nxt = smem + ((t + 1) & 1) * 2 * G::TILEB;
+    // The other buffer was last read in iteration t-1, which every wave has
+    // left (barrier below), so the next tile can stream into it now.
+    if (t + 1 < ntiles) loader.load(Kb, Vb, j0 + G::BN, N, nxt, nxt + G::TILEB);
+    tile_step16<E, D, false>(cur, cur + G::TILEB, qf, acc, m, l, j0, N, c2);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads landed
+    __syncthreads();                                     // ... and everyone's
+  }
+  if (nfull < ntiles) {
+    unsigned char* cur = smem + (nfull & 1) * 2 * G::TILEB;
+    tile_step16<E, D, true>(cur, cur + G::TILEB, qf, acc, m, l, nfull * G::BN, N, c2);
   }
 
   // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.

@@ -102,11 +102,15 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 // Value held by lane l ^ 32, combined with the lane's own by op.
 __device__ __forceinline__ float xhalf_max(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  float r;
+  __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(__uint_as_float(s[0])), "v"(__uint_as_float(s[1])));
+  return r;
 }
 __device__ __forceinline__ float xhalf_min(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  float r;
+  __asm__("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(__uint_as_float(s[0])), "v"(__uint_as_float(s[1])));
+  return r;
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -115,23 +119,40 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Row extreme over a lane's 16-value fragment.
-__device__ __forceinline__ float frag_max(const f32x16& s) {
-  float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
-  float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
-  float c = fmaxf(fmaxf(s[6], s[7]), s[8]);
-  float d = fmaxf(fmaxf(s[9], s[10]), s[11]);
-  float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
-  return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
+// v_max3_f32 / v_min3_f32 on values that come straight from MFMA or VALU
+// arithmetic (never signalling NaNs), so no canonicalising moves are needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
-__device__ __forceinline__ float frag_min(const f32x16& s) {
-  float a = fminf(fminf(s[0], s[1]), s[2]);
-  float b = fminf(fminf(s[3], s[4]), s[5]);
-  float c = fminf(fminf(s[6], s[7]), s[8]);
-  float d = fminf(fminf(s[9], s[10]), s[11]);
-  float e = fminf(fminf(s[12], s[13]), s[14]);
-  return fminf(fminf(fminf(a, b), fminf(c, d)), fminf(e, s[15]));
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  float r;
+  __asm__("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
+
+// Row extreme over two 16-value fragments (32 values).
+__device__ __forceinline__ float frag2_max(const f32x16& s, const f32x16& t) {
+  float a = max3f(s[0], s[1], s[2]), b = max3f(s[3], s[4], s[5]);
+  float c = max3f(s[6], s[7], s[8]), d = max3f(s[9], s[10], s[11]);
+  float e = max3f(s[12], s[13], s[14]), f = max3f(s[15], t[0], t[1]);
+  float g = max3f(t[2], t[3], t[4]), h = max3f(t[5], t[6], t[7]);
+  float i = max3f(t[8], t[9], t[10]), j = max3f(t[11], t[12], t[13]);
+  float k = max3f(a, b, c), m = max3f(d, e, f), n = max3f(g, h, i);
+  return max3f(max3f(k, m, n), j, fmaxf(t[14], t[15]));
+}
+__device__ __forceinline__ float frag2_min(const f32x16& s, const f32x16& t) {
+  float a = min3f(s[0], s[1], s[2]), b = min3f(s[3], s[4], s[5]);
+  float c = min3f(s[6], s[7], s[8]), d = min3f(s[9], s[10], s[11]);
+  float e = min3f(s[12], s[13], s[14]), f = min3f(s[15], t[0], t[1]);
+  float g = min3f(t[2], t[3], t[4]), h = min3f(t[5], t[6], t[7]);
+  float i = min3f(t[8], t[9], t[10]), j = min3f(t[11], t[12], t[13]);
+  float k = min3f(a, b, c), m = min3f(d, e, f), n = min3f(g, h, i);
+  return min3f(min3f(k, m, n), j, fminf(t[14], t[15]));
+}
+__device__ __forceinline__ float frag_max(const f32x16& s) { return frag2_max(s, s); }
+__device__ __forceinline__ float frag_min(const f32x16& s) { return frag2_min(s, s); }
 
 // ---------------------------------------------------------------------------
 // bf16 / fp16 kernel
@@ -167,16 +188,22 @@ typedef __attribute__((address_space(1))) void gmem_void;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Stream one K tile and one V tile (keys j0 .. j0+63) straight from global
-// memory into LDS with 16-byte direct loads (global_load_lds_dwordx4): lane i
-// of a wave-wide load fills bytes [16 i, 16 i + 16) of a 1 KiB LDS block, so
-// the swizzle is applied on the source side, by choosing which chunk each
-// lane fetches.  Every row of a tile is a contiguous 2*d-byte run of K or V,
-// read whole by CH consecutive lanes (coalesced).
+// memory into LDS with 16-byte direct loads (buffer_load_dwordx4 ... lds):
+// lane i of a wave-wide load fills bytes [16 i, 16 i + 16) of a 1 KiB LDS
+// block, so the swizzle is applied on the source side, by choosing which
+// chunk each lane fetches.  Every row of a tile is a contiguous 2*d-byte run
+// of K or V, read whole by CH consecutive lanes (coalesced).
 //
 // Load u of wave w fills block u*4 + w, i.e. rows 16u + r0 (d = 128) or
 // 32u + r0 (d = 64) with r0 = w * ROWS_PER_LOAD + lane / CH.  The swizzle
 // bits of those rows do not depend on u, so each lane's byte offset within
-// the 16/32-row group is a loop invariant and the per-load base is uniform.
+// the 16/32-row group is a loop invariant.  Each load gets a buffer
+// descriptor whose base is the group's first row and whose size covers only
+// rows < N: the hardware range check returns zeros for rows past the end of
+// the sequence (their scores are masked, and zero V rows add nothing), so no
+// load ever touches memory outside the head.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 template <int D>
 struct TileLoader {
   using G = Geo16<D>;
@@ -184,56 +211,32 @@ struct TileLoader {
   static constexpr int STEP_ROWS = NW * G::ROWS_PER_LOAD;  // rows between loads u, u+1
   static_assert(STEP_ROWS % 16 == 0, "swizzle bits must not depend on u");
   uint32_t koff, voff;  // this lane's byte offset from the group's first row
-  int r0;               // this lane's row within a group
+  int wave;             // wave index, uniform
 
   __device__ __forceinline__ TileLoader() {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    r0 = wave * G::ROWS_PER_LOAD + lane / G::CH;
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r0 = wave * G::ROWS_PER_LOAD + lane / G::CH;
     const int p = lane % G::CH;
     koff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_k<D>(r0)) << 4));
     voff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_v<D>(r0)) << 4));
   }
 
-  // Full tile: rows j0 .. j0+63 all exist.
-  __device__ __forceinline__ void full(const unsigned char* Kb, const unsigned char* Vb, int j0,
-                                       unsigned char* kb, unsigned char* vb) const {
-    const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
-      const size_t base = (size_t)(j0 + u * STEP_ROWS) * G::ROWB;
-      const int blk = u * NW + wave;
-      __builtin_amdgcn_global_load_lds((gmem_void*)(Kb + base + koff),
-                                       (lds_void*)(kb + blk * G::LOADB), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gmem_void*)(Vb + base + voff),
-                                       (lds_void*)(vb + blk * G::LOADB), 16, 0, 0);
-    }
-  }
-
-  // Last, partial tile: rows past N-1 re-read row N-1 (in bounds); their
-  // scores are masked and their probabilities are zero.
-  __device__ __forceinline__ void tail(const unsigned char* Kb, const unsigned char* Vb, int j0,
-                                       int N, unsigned char* kb, unsigned char* vb) const {
-    const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
-      const int r = u * STEP_ROWS + r0;
-      const int grow = min(j0 + r, N - 1);
-      const size_t rowbase = (size_t)grow * G::ROWB;
-      const uint32_t kc = koff - (uint32_t)(r0 * G::ROWB), vc = voff - (uint32_t)(r0 * G::ROWB);
-      const int blk = u * NW + wave;
-      __builtin_amdgcn_global_load_lds((gmem_void*)(Kb + rowbase + kc),
-                                       (lds_void*)(kb + blk * G::LOADB), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gmem_void*)(Vb + rowbase + vc),
-                                       (lds_void*)(vb + blk * G::LOADB), 16, 0, 0);
-    }
-  }
-
   __device__ __forceinline__ void load(const unsigned char* Kb, const unsigned char* Vb, int j0,
                                        int N, unsigned char* kb, unsigned char* vb) const {
-    if (j0 + G::BN <= N)
-      full(Kb, Vb, j0, kb, vb);
-    else
-      tail(Kb, Vb, j0, N, kb, vb);
+#pragma unroll
+    for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
+      const int row = j0 + u * STEP_ROWS;
+      const size_t base = (size_t)row * G::ROWB;
+      const int bytes = N > row ? (N - row) * G::ROWB : 0;  // N*ROWB < 2^31
+      const int blk = u * NW + wave;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + base), (short)0, bytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Vb + base), (short)0, bytes, kBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kb + blk * G::LOADB), 16, koff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vb + blk * G::LOADB), 16, voff, 0, 0, 0);
+    }
   }
 };
 
@@ -283,9 +286,9 @@ __device__ __forceinline__ void tile_step16(const unsigned char* kb, const unsig
   // comes from the min of s).
   float mt;
   if (c2 >= 0.f) {
-    mt = xhalf_max(fmaxf(frag_max(s[0]), frag_max(s[1])));
+    mt = xhalf_max(frag2_max(s[0], s[1]));
   } else {
-    mt = xhalf_min(fminf(frag_min(s[0]), frag_min(s[1])));
+    mt = xhalf_min(frag2_min(s[0], s[1]));
   }
   const float m_tile = mt * c2;
   if (__builtin_amdgcn_ballot_w64(m_tile > m + kRescaleThreshold) != 0) {  // wave-uniform
@@ -395,21 +398,28 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Full tiles in the loop; the one partial tile (if N % 64 != 0) after it.
-  const int nfull = N / G::BN;
-  for (int t = 0; t < nfull; ++t) {
+  // Full tiles in the loop (two per trip, so that each buffer's LDS
+  // addresses are constants); the one partial tile (N % 64 != 0) after it.
+  unsigned char* const buf0 = smem;
+  unsigned char* const buf1 = smem + 2 * G::TILEB;
+  auto step = [&](int t, unsigned char* cur, unsigned char* nxt) {
     const int j0 = t * G::BN;
-    unsigned char* cur = smem + (t & 1) * 2 * G::TILEB;
-    unsigned char* nxt = smem + ((t + 1) & 1) * 2 * G::TILEB;
     // The other buffer was last read in iteration t-1, which every wave has
     // left (barrier below), so the next tile can stream into it now.
     if (t + 1 < ntiles) loader.load(Kb, Vb, j0 + G::BN, N, nxt, nxt + G::TILEB);
     tile_step16<E, D, false>(cur, cur + G::TILEB, qf, acc, m, l, j0, N, c2);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads landed
     __syncthreads();                                     // ... and everyone's
+  };
+  const int nfull = N / G::BN;
+  int t = 0;
+  for (; t + 2 <= nfull; t += 2) {
+    step(t, buf0, buf1);
+    step(t + 1, buf1, buf0);
   }
+  if (t < nfull) step(t++, buf0, buf1);
   if (nfull < ntiles) {
-    unsigned char* cur = smem + (nfull & 1) * 2 * G::TILEB;
+    unsigned char* cur = (nfull & 1) ? buf1 : buf0;
     tile_step16<E, D, true>(cur, cur + G::TILEB, qf, acc, m, l, nfull * G::BN, N, c2);
   }
 

@@ -48,8 +48,9 @@ enum {
   ATTN_ERR_HIP = -8       /* the kernel launch failed (hipGetLastError)         */
 };
 
-/* Largest sequence length accepted: per-head offsets are 32-bit in-kernel. */
-#define ATTN_MAX_N (1 << 24)
+/* Largest sequence length accepted: per-head byte offsets and buffer sizes
+ * are 32-bit in-kernel (N * 2d bytes must stay below 2^31). */
+#define ATTN_MAX_N (1 << 22)
 
 /*
  * attn_fwd - O = softmax(scale * Q K^T) V and lse, for all B*H heads.

@@ -72,7 +72,7 @@ def call(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=128, d=64, scale=0.125, dty
     (dict(o=None), NULLPTR),
     (dict(q=Q + 8), ALIGN), (dict(o=O + 2), ALIGN), (dict(v=V + 4), ALIGN), (dict(lse=L + 2), ALIGN),
     (dict(o=Q), ALIAS), (dict(o=K + 64), ALIAS), (dict(lse=V), ALIAS), (dict(lse=O + 16), ALIAS),
-    (dict(N=(1 << 24) + 1), SHAPE),
+    (dict(N=(1 << 22) + 1), SHAPE),
     (dict(B=1 << 40, H=1 << 30), SHAPE),
 ])
 def test_rejects_before_any_hip_call(lib, kw, code):

@@ -204,6 +204,33 @@ typedef __attribute__((address_space(3))) void lds_void;
 // load ever touches memory outside the head.
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor: base, stride 0, size in bytes (the range check), word 3.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  return (i32x4){(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferWord3};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)(p);
+}
+
+// One wave-wide 16-byte-per-lane load into LDS at lds (uniform) + 16 * lane.
+// Written as inline asm on purpose: the compiler cannot tell which LDS bytes
+// a DMA load writes, and for the builtin it waits for every outstanding load
+// before the next LDS read of ANY buffer, which would expose the full load
+// latency once per tile.  Here completion is awaited explicitly
+// (s_waitcnt vmcnt(0)) before the barrier that publishes a tile, and no
+// buffer is read while a load into it is in flight.  M0 holds the LDS base;
+// nothing else in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "s"(lds)
+                   : "memory");
+}
+
 template <int D>
 struct TileLoader {
   using G = Geo16<D>;
@@ -222,43 +249,39 @@ struct TileLoader {
     voff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_v<D>(r0)) << 4));
   }
 
-  __device__ __forceinline__ void load(const unsigned char* Kb, const unsigned char* Vb, int j0,
-                                       int N, unsigned char* kb, unsigned char* vb) const {
+  // Rows j0 .. j0+63 of one tensor (K or V, with its lane offset) -> xb.
+  __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int j0, int N,
+                                       unsigned char* xb) const {
 #pragma unroll
     for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
       const int row = j0 + u * STEP_ROWS;
-      const size_t base = (size_t)row * G::ROWB;
       const int bytes = N > row ? (N - row) * G::ROWB : 0;  // N*ROWB < 2^31
       const int blk = u * NW + wave;
-      const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + base), (short)0, bytes, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(Vb + base), (short)0, bytes, kBufferWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kb + blk * G::LOADB), 16, koff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vb + blk * G::LOADB), 16, voff, 0, 0, 0);
+      lds_dma16(buffer_rsrc(Xb + (size_t)row * G::ROWB, bytes), off,
+                lds_addr(xb + blk * G::LOADB));
     }
+  }
+  __device__ __forceinline__ void load_k(const unsigned char* Kb, int j0, int N,
+                                         unsigned char* kb) const {
+    load(Kb, koff, j0, N, kb);
+  }
+  __device__ __forceinline__ void load_v(const unsigned char* Vb, int j0, int N,
+                                         unsigned char* vb) const {
+    load(Vb, voff, j0, N, vb);
   }
 };
 
-// The reference max m (log2 domain) moves only when some row of the wave
-// exceeds it by more than this many doublings; until then P = 2^(t - m) may
-// reach 2^8, harmless in fp32 and in bf16/fp16 (same relative precision).
-// The result is the same softmax: O = acc / l with acc and l built from the
-// same reference.
-constexpr float kRescaleThreshold = 8.0f;
+// --- pieces of one K/V tile -------------------------------------------------
 
-// One K/V tile: scores, online-softmax update, P.V accumulate.
-template <class E, int D, bool TAIL>
-__device__ __forceinline__ void tile_step16(const unsigned char* kb, const unsigned char* vb,
-                                            const u32x4 (&qf)[Geo16<D>::KS],
-                                            f32x16 (&acc)[Geo16<D>::DB], float& m, float& l,
-                                            int j0, int N, float c2) {
+// S^T = K Q^T for the two 32-key halves of a 64-key tile.  s[sb][r] is the
+// raw score of key 32 sb + 8 (r/4) + 4 hh + r%4 (tile-relative) for query row
+// li of the wave, hh = lane / 32.
+template <class E, int D>
+__device__ __forceinline__ void qk16(const unsigned char* kb, const u32x4 (&qf)[Geo16<D>::KS],
+                                     f32x16 (&s)[2]) {
   using G = Geo16<D>;
   const int lane = threadIdx.x & 63;
   const int li = lane & 31, hh = lane >> 5;
-
-  // S^T = K Q^T for two 32-key halves of the tile.
-  f32x16 s[2];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     s[sb] = (f32x16){};
@@ -271,69 +294,87 @@ __device__ __forceinline__ void tile_step16(const unsigned char* kb, const unsig
       s[sb] = E::mfma(a, qf[ks], s[sb]);
     }
   }
-  // s[sb][r] is the raw score of key j0 + 32 sb + 8 (r/4) + 4 hh + r%4.
+}
 
-  if (TAIL) {  // keys >= N: neutral for the row extreme
-    const float neutral = c2 >= 0.f ? -INFINITY : INFINITY;
+// Keys >= N in the last, partial tile: a value that cannot win the row
+// extreme (the probabilities of these keys are zeroed in softmax16).
+__device__ __forceinline__ void mask_tail16(f32x16 (&s)[2], int j0, int N, float c2) {
+  const int hh = (threadIdx.x & 63) >> 5;
+  const float neutral = c2 >= 0.f ? -INFINITY : INFINITY;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+  for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N) s[sb][r] = neutral;
-  }
+    for (int r = 0; r < 16; ++r)
+      if (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N) s[sb][r] = neutral;
+}
 
-  // Tile max of the log2-scaled scores t = s * c2 (for c2 < 0 the max of t
-  // comes from the min of s).
-  float mt;
-  if (c2 >= 0.f) {
-    mt = xhalf_max(frag2_max(s[0], s[1]));
-  } else {
-    mt = xhalf_min(frag2_min(s[0], s[1]));
-  }
-  const float m_tile = mt * c2;
+// Row max of the log2-scaled scores t = s * c2 over the tile (for c2 < 0 the
+// max of t comes from the min of s); both lane halves get the row's value.
+__device__ __forceinline__ float tile_max16(const f32x16 (&s)[2], float c2) {
+  const float mt = c2 >= 0.f ? xhalf_max(frag2_max(s[0], s[1])) : xhalf_min(frag2_min(s[0], s[1]));
+  return mt * c2;
+}
+
+// The reference max m (log2 domain) moves only when some row of the wave
+// exceeds it by more than this many doublings; until then P = 2^(t - m) may
+// reach 2^8, harmless in fp32 and in bf16/fp16 (same relative precision).
+// The result is the same softmax: O = acc / l with acc and l built from the
+// same reference.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D>
+__device__ __forceinline__ void maybe_rescale(float m_tile, float& m, float& l,
+                                              f32x16 (&acc)[Geo16<D>::DB]) {
   if (__builtin_amdgcn_ballot_w64(m_tile > m + kRescaleThreshold) != 0) {  // wave-uniform
     const float m_new = fmaxf(m, m_tile);
-    const float alpha = fast_exp2(m - m_new);  // m = -inf on the first tile -> 0
+    const float alpha = fast_exp2(m - m_new);
     m = m_new;
     l *= alpha;
 #pragma unroll
-    for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
+    for (int db = 0; db < Geo16<D>::DB; ++db) acc[db] *= alpha;
   }
+}
 
-  // P = 2^(t - m); the row sum takes the fp32 values (the log-sum-exp output
-  // depends on it directly), the MFMA takes them rounded to the element type.
-  u32x4 pb[2][2];
+// P = 2^(s * c2 - m), packed to the element type (RNE) as the B operand of
+// the P.V product; returns this lane's fp32 row-sum contribution (the
+// log-sum-exp output depends on it directly, so it sums unrounded values).
+template <class E, bool TAIL>
+__device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float c2,
+                                           u32x4 (&pb)[2][2], int j0, int N) {
+  const int hh = (threadIdx.x & 63) >> 5;
   float rs = 0.f;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
+    float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(fmaf(s[sb][r], c2, -m));
-      if (TAIL && (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N)) p = 0.f;
-      s[sb][r] = p;
-      rs += p;
+      p[r] = fast_exp2(fmaf(s[sb][r], c2, -m));
+      if (TAIL && (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N)) p[r] = 0.f;
+      rs += p[r];
     }
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
       const int b0 = 8 * hq;
-      pb[sb][hq] = (u32x4){E::pack2(s[sb][b0 + 0], s[sb][b0 + 1]),
-                           E::pack2(s[sb][b0 + 2], s[sb][b0 + 3]),
-                           E::pack2(s[sb][b0 + 4], s[sb][b0 + 5]),
-                           E::pack2(s[sb][b0 + 6], s[sb][b0 + 7])};
+      pb[sb][hq] = (u32x4){E::pack2(p[b0 + 0], p[b0 + 1]), E::pack2(p[b0 + 2], p[b0 + 3]),
+                           E::pack2(p[b0 + 4], p[b0 + 5]), E::pack2(p[b0 + 6], p[b0 + 7])};
     }
   }
-  l += rs;
+  return rs;
+}
 
-  // O^T += V^T P^T, 16 keys per MFMA.
-  const int p16 = lane & 15;
-  const int colhalf = (lane >> 4) & 1;
+// O^T += V^T P^T, 16 keys per MFMA; V^T comes from transposing LDS reads:
+// lane (p16, group) points at row key0 + p16/4, columns c0 + 4*(p16%4) .. +3,
+// and receives column c0 + p16 of rows key0 .. key0+3.
+template <class E, int D>
+__device__ __forceinline__ void pv16(const unsigned char* vb, const u32x4 (&pb)[2][2],
+                                     f32x16 (&acc)[Geo16<D>::DB]) {
+  using G = Geo16<D>;
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5, p16 = lane & 15, colhalf = (lane >> 4) & 1;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
-      // Transposing reads: lane (p16, group) points at row key0 + p16/4,
-      // columns c0 + 4*(p16%4) .. +3; it receives column c0 + p16 of rows
-      // key0 .. key0+3.
       const int r0 = 32 * sb + 16 * hq + 4 * hh + (p16 >> 2);
       const int r1 = r0 + 8;
       const int half8 = (p16 & 1) * 8;
@@ -353,6 +394,15 @@ __device__ __forceinline__ void tile_step16(const unsigned char* kb, const unsig
   }
 }
 
+// --- the kernel ---------------------------------------------------------------
+//
+// Software pipeline over key tiles.  Iteration t holds the scores S_t of tile
+// t in registers and, in one straight-line block, turns S_t into P_t (VALU),
+// computes S_{t+1} = K_{t+1} Q^T (MFMA, independent of P_t, so the two
+// interleave) and accumulates P_t V_t (MFMA); then it takes the row max of
+// S_{t+1} and, rarely, rescales.  K therefore runs one tile ahead of V:
+// iteration t reads K_{t+1} and V_t while K_{t+2} and V_{t+1} stream into
+// the other K and V buffers.
 template <class E, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -360,6 +410,10 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      float* __restrict__ LSE, int N, int nqt, float c2) {
   using G = Geo16<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM];
+  unsigned char* const kbuf0 = smem;
+  unsigned char* const kbuf1 = smem + G::TILEB;
+  unsigned char* const vbuf0 = smem + 2 * G::TILEB;
+  unsigned char* const vbuf1 = smem + 3 * G::TILEB;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hh = lane >> 5;
@@ -367,60 +421,76 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / nqt, qt = tile - bh * nqt;
   const size_t hoff = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + hoff;
-  const uint16_t* Kh = K + hoff;
-  const uint16_t* Vh = V + hoff;
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + hoff);
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
 
   const int ntiles = (N + G::BN - 1) / G::BN;
-  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(Kh);
-  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(Vh);
   const TileLoader<D> loader;
-  loader.load(Kb, Vb, 0, N, smem, smem + G::TILEB);
+  loader.load_k(Kb, 0, N, kbuf0);
+  loader.load_v(Vb, 0, N, vbuf0);
+  if (ntiles > 1) loader.load_k(Kb, G::BN, N, kbuf1);
 
   // Q fragment, resident for the whole key loop: lane (li, hh) holds
   // d = 16 ks + 8 hh + [0, 8) of query row qrow.
   const int qrow = qt * G::BM + wave * 32 + li;
   u32x4 qf[G::KS];
   if (qrow < N) {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 8 * hh);
+    const u32x4* qp = reinterpret_cast<const u32x4*>(Q + hoff + (size_t)qrow * D + 8 * hh);
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) qf[ks] = qp[2 * ks];
   } else {
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) qf[ks] = (u32x4){0u, 0u, 0u, 0u};
   }
-
   f32x16 acc[G::DB];
 #pragma unroll
   for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
-  float m = -INFINITY, l = 0.f;
+  float l = 0.f;
 
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Full tiles in the loop (two per trip, so that each buffer's LDS
-  // addresses are constants); the one partial tile (N % 64 != 0) after it.
-  unsigned char* const buf0 = smem;
-  unsigned char* const buf1 = smem + 2 * G::TILEB;
-  auto step = [&](int t, unsigned char* cur, unsigned char* nxt) {
-    const int j0 = t * G::BN;
-    // The other buffer was last read in iteration t-1, which every wave has
-    // left (barrier below), so the next tile can stream into it now.
-    if (t + 1 < ntiles) loader.load(Kb, Vb, j0 + G::BN, N, nxt, nxt + G::TILEB);
-    tile_step16<E, D, false>(cur, cur + G::TILEB, qf, acc, m, l, j0, N, c2);
+  f32x16 sA[2], sB[2];
+  qk16<E, D>(kbuf0, qf, sA);
+  if (G::BN > N) mask_tail16(sA, 0, N, c2);
+  float m = tile_max16(sA, c2);  // the first tile sets the reference exactly
+  __syncthreads();               // kbuf0 is free for K_2 only after every wave read K_0
+
+  auto body = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], const unsigned char* kb_next,
+                  const unsigned char* vb_cur, unsigned char* kb_load, unsigned char* vb_load) {
+    const int j1 = (t + 1) * G::BN;
+    if (t + 2 < ntiles) loader.load_k(Kb, j1 + G::BN, N, kb_load);
+    loader.load_v(Vb, j1, N, vb_load);
+    u32x4 pb[2][2];
+    l += softmax16<E, false>(cur, m, c2, pb, 0, N);  // tiles before the last are full
+    qk16<E, D>(kb_next, qf, nxt);
+    pv16<E, D>(vb_cur, pb, acc);
+    if (j1 + G::BN > N) mask_tail16(nxt, j1, N, c2);
+    maybe_rescale<D>(tile_max16(nxt, c2), m, l, acc);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads landed
     __syncthreads();                                     // ... and everyone's
   };
-  const int nfull = N / G::BN;
+  auto last = [&](int t, const f32x16 (&cur)[2], const unsigned char* vb_cur) {
+    u32x4 pb[2][2];
+    const int j0 = t * G::BN;
+    if (j0 + G::BN > N)
+      l += softmax16<E, true>(cur, m, c2, pb, j0, N);
+    else
+      l += softmax16<E, false>(cur, m, c2, pb, j0, N);
+    pv16<E, D>(vb_cur, pb, acc);
+  };
+
+  // Two iterations per trip so that every LDS address is a constant.
   int t = 0;
-  for (; t + 2 <= nfull; t += 2) {
-    step(t, buf0, buf1);
-    step(t + 1, buf1, buf0);
+  for (; t + 2 < ntiles; t += 2) {
+    body(t, sA, sB, kbuf1, vbuf0, kbuf0, vbuf1);
+    body(t + 1, sB, sA, kbuf0, vbuf1, kbuf1, vbuf0);
   }
-  if (t < nfull) step(t++, buf0, buf1);
-  if (nfull < ntiles) {
-    unsigned char* cur = (nfull & 1) ? buf1 : buf0;
-    tile_step16<E, D, true>(cur, cur + G::TILEB, qf, acc, m, l, nfull * G::BN, N, c2);
+  if (t + 1 < ntiles) {
+    body(t, sA, sB, kbuf1, vbuf0, kbuf0, vbuf1);
+    last(t + 1, sB, vbuf1);
+  } else {
+    last(t, sA, vbuf0);
   }
 
   // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.

@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "attn_fwd.h"
 
@@ -55,6 +57,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -119,6 +122,17 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that is also a hard scheduling fence: no instruction
+// (MFMA, VALU, LDS read or DMA load) may be moved across it by the compiler.
+// The buffer-reuse protocol of the kernels relies on loads staying on their
+// side of a barrier, and the ping-pong schedule relies on phases staying in
+// their slots.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // v_max3_f32 / v_min3_f32 on values that come straight from MFMA or VALU
 // arithmetic (never signalling NaNs), so no canonicalising moves are needed.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -157,19 +171,18 @@ __device__ __forceinline__ float frag_min(const f32x16& s) { return frag2_min(s,
 // ---------------------------------------------------------------------------
 // bf16 / fp16 kernel
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NWAVES = 4>
 struct Geo16 {
-  static constexpr int BM = 128;               // query rows per block
   static constexpr int BN = 64;                // keys per LDS tile
   static constexpr int ROWB = D * 2;           // bytes per K/V row
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int TILEB = BN * ROWB;      // bytes of one K or V tile
   static constexpr int KS = D / 16;            // k-steps of K*Q^T
   static constexpr int DB = D / 32;            // 32-wide column blocks of O
-  static constexpr int SMEM = 4 * TILEB;       // K,V x 2 buffers
   static constexpr int LOADB = 64 * 16;        // bytes one wave-wide 16-byte load moves
   static constexpr int ROWS_PER_LOAD = LOADB / ROWB;
-  static constexpr int LOADS_PER_WAVE = TILEB / LOADB / (kThreads / 64);
+  static constexpr int LOADS_PER_WAVE = TILEB / LOADB / NWAVES;
+  static_assert(LOADS_PER_WAVE >= 1, "every wave loads at least one block");
 };
 
 // LDS swizzles: physical 16-byte chunk = logical chunk ^ f(row).
@@ -194,8 +207,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // chunk each lane fetches.  Every row of a tile is a contiguous 2*d-byte run
 // of K or V, read whole by CH consecutive lanes (coalesced).
 //
-// Load u of wave w fills block u*4 + w, i.e. rows 16u + r0 (d = 128) or
-// 32u + r0 (d = 64) with r0 = w * ROWS_PER_LOAD + lane / CH.  The swizzle
+// With NWAVES issuing waves, load u of issuing wave w fills block
+// u * NWAVES + w, i.e. rows u * STEP_ROWS + r0 with r0 = w * ROWS_PER_LOAD +
+// lane / CH and STEP_ROWS a multiple of 16.  The swizzle
 // bits of those rows do not depend on u, so each lane's byte offset within
 // the 16/32-row group is a loop invariant.  Each load gets a buffer
 // descriptor whose base is the group's first row and whose size covers only
@@ -212,8 +226,12 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes) {
   return (i32x4){(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, kBufferWord3};
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lds_void*)(p);
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// LDS byte offset of an LDS pointer (a compile-time constant plus offsets
+// when the pointer derives from a __shared__ array).
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) {
+  return (uint32_t)(uintptr_t)(p);
 }
 
 // One wave-wide 16-byte-per-lane load into LDS at lds (uniform) + 16 * lane.
@@ -231,18 +249,17 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t ld
                    : "memory");
 }
 
-template <int D>
+template <int D, int NWAVES>
 struct TileLoader {
-  using G = Geo16<D>;
-  static constexpr int NW = kThreads / 64;
+  using G = Geo16<D, NWAVES>;
+  static constexpr int NW = NWAVES;
   static constexpr int STEP_ROWS = NW * G::ROWS_PER_LOAD;  // rows between loads u, u+1
   static_assert(STEP_ROWS % 16 == 0, "swizzle bits must not depend on u");
   uint32_t koff, voff;  // this lane's byte offset from the group's first row
-  int wave;             // wave index, uniform
+  int wave;             // index of the issuing wave among the NWAVES, uniform
 
-  __device__ __forceinline__ TileLoader() {
+  __device__ __forceinline__ explicit TileLoader(int w) : wave(w) {
     const int lane = threadIdx.x & 63;
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r0 = wave * G::ROWS_PER_LOAD + lane / G::CH;
     const int p = lane % G::CH;
     koff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_k<D>(r0)) << 4));
@@ -251,7 +268,7 @@ struct TileLoader {
 
   // Rows j0 .. j0+63 of one tensor (K or V, with its lane offset) -> xb.
   __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int j0, int N,
-                                       unsigned char* xb) const {
+                                       lds_u8* xb) const {
 #pragma unroll
     for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
       const int row = j0 + u * STEP_ROWS;
@@ -262,11 +279,11 @@ struct TileLoader {
     }
   }
   __device__ __forceinline__ void load_k(const unsigned char* Kb, int j0, int N,
-                                         unsigned char* kb) const {
+                                         lds_u8* kb) const {
     load(Kb, koff, j0, N, kb);
   }
   __device__ __forceinline__ void load_v(const unsigned char* Vb, int j0, int N,
-                                         unsigned char* vb) const {
+                                         lds_u8* vb) const {
     load(Vb, voff, j0, N, vb);
   }
 };
@@ -277,7 +294,7 @@ struct TileLoader {
 // raw score of key 32 sb + 8 (r/4) + 4 hh + r%4 (tile-relative) for query row
 // li of the wave, hh = lane / 32.
 template <class E, int D>
-__device__ __forceinline__ void qk16(const unsigned char* kb, const u32x4 (&qf)[Geo16<D>::KS],
+__device__ __forceinline__ void qk16(const lds_u8* kb, const u32x4 (&qf)[Geo16<D>::KS],
                                      f32x16 (&s)[2]) {
   using G = Geo16<D>;
   const int lane = threadIdx.x & 63;
@@ -286,11 +303,11 @@ __device__ __forceinline__ void qk16(const unsigned char* kb, const u32x4 (&qf)[
   for (int sb = 0; sb < 2; ++sb) {
     s[sb] = (f32x16){};
     const int row = sb * 32 + li;
-    const unsigned char* rp = kb + row * G::ROWB;
+    const lds_u8* rp = kb + row * G::ROWB;
     const int sw = swz_k<D>(row);
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(rp + (((2 * ks + hh) ^ sw) << 4));
+      const u32x4 a = *(const lds_u32x4*)(rp + (((2 * ks + hh) ^ sw) << 4));
       s[sb] = E::mfma(a, qf[ks], s[sb]);
     }
   }
@@ -342,7 +359,10 @@ template <class E, bool TAIL>
 __device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float c2,
                                            u32x4 (&pb)[2][2], int j0, int N) {
   const int hh = (threadIdx.x & 63) >> 5;
-  float rs = 0.f;
+  // Eight independent partial sums: a single running sum would be a chain
+  // of 32 dependent adds, whose latency nothing hides when one wave of the
+  // SIMD is in its softmax phase.
+  float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     float p[16];
@@ -350,7 +370,7 @@ __device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float 
     for (int r = 0; r < 16; ++r) {
       p[r] = fast_exp2(fmaf(s[sb][r], c2, -m));
       if (TAIL && (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N)) p[r] = 0.f;
-      rs += p[r];
+      part[r & 7] += p[r];
     }
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
@@ -359,14 +379,14 @@ __device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float 
                            E::pack2(p[b0 + 4], p[b0 + 5]), E::pack2(p[b0 + 6], p[b0 + 7])};
     }
   }
-  return rs;
+  return ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
 }
 
 // O^T += V^T P^T, 16 keys per MFMA; V^T comes from transposing LDS reads:
 // lane (p16, group) points at row key0 + p16/4, columns c0 + 4*(p16%4) .. +3,
 // and receives column c0 + p16 of rows key0 .. key0+3.
 template <class E, int D>
-__device__ __forceinline__ void pv16(const unsigned char* vb, const u32x4 (&pb)[2][2],
+__device__ __forceinline__ void pv16(const lds_u8* vb, const u32x4 (&pb)[2][2],
                                      f32x16 (&acc)[Geo16<D>::DB]) {
   using G = Geo16<D>;
   const int lane = threadIdx.x & 63;
@@ -381,8 +401,8 @@ __device__ __forceinline__ void pv16(const unsigned char* vb, const u32x4 (&pb)[
 #pragma unroll
       for (int db = 0; db < G::DB; ++db) {
         const int chunk = 4 * db + 2 * colhalf + ((p16 & 3) >> 1);
-        const unsigned char* a0 = vb + r0 * G::ROWB + ((chunk ^ swz_v<D>(r0)) << 4) + half8;
-        const unsigned char* a1 = vb + r1 * G::ROWB + ((chunk ^ swz_v<D>(r1)) << 4) + half8;
+        const lds_u8* a0 = vb + r0 * G::ROWB + ((chunk ^ swz_v<D>(r0)) << 4) + half8;
+        const lds_u8* a1 = vb + r1 * G::ROWB + ((chunk ^ swz_v<D>(r1)) << 4) + half8;
         const u32x2 lo = __builtin_bit_cast(
             u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
         const u32x2 hi = __builtin_bit_cast(
@@ -408,12 +428,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, int N, int nqt, float c2) {
-  using G = Geo16<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM];
-  unsigned char* const kbuf0 = smem;
-  unsigned char* const kbuf1 = smem + G::TILEB;
-  unsigned char* const vbuf0 = smem + 2 * G::TILEB;
-  unsigned char* const vbuf1 = smem + 3 * G::TILEB;
+  using G = Geo16<D, 4>;
+  constexpr int BM = 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
+  lds_u8* const lsm = (lds_u8*)smem;
+  lds_u8* const kbuf0 = lsm;
+  lds_u8* const kbuf1 = lsm + G::TILEB;
+  lds_u8* const vbuf0 = lsm + 2 * G::TILEB;
+  lds_u8* const vbuf1 = lsm + 3 * G::TILEB;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hh = lane >> 5;
@@ -425,14 +447,14 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
 
   const int ntiles = (N + G::BN - 1) / G::BN;
-  const TileLoader<D> loader;
+  const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
   loader.load_k(Kb, 0, N, kbuf0);
   loader.load_v(Vb, 0, N, vbuf0);
   if (ntiles > 1) loader.load_k(Kb, G::BN, N, kbuf1);
 
   // Q fragment, resident for the whole key loop: lane (li, hh) holds
   // d = 16 ks + 8 hh + [0, 8) of query row qrow.
-  const int qrow = qt * G::BM + wave * 32 + li;
+  const int qrow = qt * BM + wave * 32 + li;
   u32x4 qf[G::KS];
   if (qrow < N) {
     const u32x4* qp = reinterpret_cast<const u32x4*>(Q + hoff + (size_t)qrow * D + 8 * hh);
@@ -448,16 +470,16 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   float l = 0.f;
 
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  block_barrier();
 
   f32x16 sA[2], sB[2];
   qk16<E, D>(kbuf0, qf, sA);
   if (G::BN > N) mask_tail16(sA, 0, N, c2);
   float m = tile_max16(sA, c2);  // the first tile sets the reference exactly
-  __syncthreads();               // kbuf0 is free for K_2 only after every wave read K_0
+  block_barrier();               // kbuf0 is free for K_2 only after every wave read K_0
 
-  auto body = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], const unsigned char* kb_next,
-                  const unsigned char* vb_cur, unsigned char* kb_load, unsigned char* vb_load) {
+  auto body = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], const lds_u8* kb_next,
+                  const lds_u8* vb_cur, lds_u8* kb_load, lds_u8* vb_load) {
     const int j1 = (t + 1) * G::BN;
     if (t + 2 < ntiles) loader.load_k(Kb, j1 + G::BN, N, kb_load);
     loader.load_v(Vb, j1, N, vb_load);
@@ -468,9 +490,9 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (j1 + G::BN > N) mask_tail16(nxt, j1, N, c2);
     maybe_rescale<D>(tile_max16(nxt, c2), m, l, acc);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads landed
-    __syncthreads();                                     // ... and everyone's
+    block_barrier();                                     // ... and everyone's
   };
-  auto last = [&](int t, const f32x16 (&cur)[2], const unsigned char* vb_cur) {
+  auto last = [&](int t, const f32x16 (&cur)[2], const lds_u8* vb_cur) {
     u32x4 pb[2][2];
     const int j0 = t * G::BN;
     if (j0 + G::BN > N)
@@ -494,6 +516,274 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 
   // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.
+  const float lt = xhalf_sum(l);
+  const float inv = 1.0f / lt;
+  if (qrow < N) {
+    uint16_t* op = O + hoff + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * hh;
+        const u32x2 w = (u32x2){E::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                                E::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + col) = w;
+      }
+    if (LSE != nullptr && hh == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+  }
+}
+
+// --- MFMA phase with lean registers ---------------------------------------
+//
+// acc += P V (from vb) followed by S^T = K Q^T (from kb), for the ping-pong
+// kernel.  LDS addresses: with the XOR swizzles above, the address of K
+// fragment (sb, ks) is (kq ^ (ks << 5)) + sb * 32 * ROWB and that of V^T
+// fragment (sb, hq, db, half) is (vq ^ (db << 6)) + (32 sb + 16 hq + 8 half)
+// * ROWB, with kq, vq per-lane constants (the XORed bits of kq / vq are the
+// swizzle bits, the row parts are multiples of ROWB), so each needs one base
+// register and one v_xor per ks / db instead of a register per fragment.
+// The LDS reads are scheduled a fixed LA MFMAs ahead of their use.
+template <int D>
+struct LdsLanes {
+  uint32_t kq, vq;
+  __device__ __forceinline__ LdsLanes() {
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 31, hh = lane >> 5, p16 = lane & 15;
+    constexpr int ROWB = D * 2;
+    kq = (uint32_t)(li * ROWB + ((hh ^ swz_k<D>(li)) << 4));
+    const int rowpart = 4 * hh + (p16 >> 2);
+    const int cb = 2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1);
+    vq = (uint32_t)(rowpart * ROWB + 16 * cb + (p16 & 1) * 8 + ((swz_v<D>(rowpart) >> 2) << 6));
+  }
+};
+
+template <class E, int D>
+__device__ __forceinline__ void mfma_phase(const lds_u8* kb, const lds_u8* vb, LdsLanes<D> ln,
+                                           bool with_pv, const u32x4 (&pb)[2][2],
+                                           f32x16 (&acc)[Geo16<D>::DB],
+                                           const u32x4 (&qf)[Geo16<D>::KS], f32x16 (&s)[2]) {
+  using G = Geo16<D>;
+  constexpr int ROWB = G::ROWB;
+  // The MFMA phase runs at raised wave priority, so that when the other wave
+  // of the SIMD (in its VALU phase) also has instructions ready, the MFMAs,
+  // each of which keeps the matrix pipe busy for many cycles, issue first.
+  __builtin_amdgcn_s_setprio(3);
+  // Fresh copies each phase, so the per-fragment XORs stay inside the loop.
+  uint32_t kq = ln.kq, vq = ln.vq;
+  __asm__ volatile("" : "+v"(kq), "+v"(vq));
+  if (with_pv) {
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+      const lds_u8* va = vb + (vq ^ (uint32_t)(db << 6));
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+          const lds_u8* a0 = va + (32 * sb + 16 * hq) * ROWB;
+          const u32x2 lo = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
+          const u32x2 hi = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * ROWB)));
+          acc[db] = E::mfma((u32x4){lo[0], lo[1], hi[0], hi[1]}, pb[sb][hq], acc[db]);
+        }
+    }
+  }
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) {
+    const lds_u8* ka = kb + (kq ^ (uint32_t)(ks << 5));
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const u32x4 a = *(const lds_u32x4*)(ka + sb * 32 * ROWB);
+      s[sb] = E::mfma(a, qf[ks], s[sb]);
+    }
+  }
+  // Schedule: LDS reads run LA MFMAs ahead of the MFMA that consumes them.
+  constexpr int LA = 4, NPV = 4 * G::DB, NQK = 2 * G::KS;
+  constexpr int DSR = 0x100, MFMA = 0x008;
+  if (with_pv) {
+    __builtin_amdgcn_sched_group_barrier(DSR, 2 * LA, 0);
+#pragma unroll
+    for (int i = 0; i < NPV - LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(DSR, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+    }
+  } else {
+    __builtin_amdgcn_sched_group_barrier(DSR, LA, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NQK - LA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(DSR, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(MFMA, LA, 0);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// --- ping-pong kernel ----------------------------------------------------------
+//
+// 8 waves = 256 query rows per block, in two groups of 4 waves; waves w and
+// w + 4 run on the same SIMD.  Per key tile each wave has an MFMA phase
+// (acc += P_{t-1} V_{t-1}, then S_t = K_t Q^T: 2 x 16 MFMAs) and a VALU phase
+// (row max, rare rescale, P_t = 2^(t - m), row sum).  Execution proceeds in
+// barrier-separated slots; group 1 runs one slot behind group 0, so in every
+// slot one wave of each SIMD issues MFMAs while the other issues the VALU
+// work that the MFMA pipe cannot do, instead of both competing for the same
+// unit at the same time.
+//
+// Slot k (every wave passes the same barriers): the work item of group g is
+// i = k - g; for 0 <= i < 2T item i is phase (i % 2) of tile i / 2, item 2T
+// is the final P_{T-1} V_{T-1}.  At even slots k = 2t the waves of group 1
+// (then in their VALU phase) start the loads of K_{t+1} and V_t; they await
+// them at the end of slot 2t + 1, in time for the first reader in slot 2t + 2.  Buffer reuse: K_{t+1} and V_t
+// overwrite K_{t-1} and V_{t-2}, whose last readers (phase 0 of tile t-1)
+// finished in slot 2t - 1.
+constexpr int kPPThreads = 512;
+
+template <class E, int D>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                   float* __restrict__ LSE, int N, int nqt, float c2) {
+  using G = Geo16<D, 8>;
+  constexpr int BM = 256;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
+  lds_u8* const lsm = (lds_u8*)smem;
+  lds_u8* const kbuf0 = lsm;
+  lds_u8* const kbuf1 = lsm + G::TILEB;
+  lds_u8* const vbuf0 = lsm + 2 * G::TILEB;
+  lds_u8* const vbuf1 = lsm + 3 * G::TILEB;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;
+  const int li = lane & 31, hh = lane >> 5;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / nqt, qt = tile - bh * nqt;
+  const size_t hoff = (size_t)bh * N * D;
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + hoff);
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
+
+  const int T = (N + G::BN - 1) / G::BN;
+  // Only the waves of group 1 issue tile loads: they are in their VALU phase
+  // at every even slot, so the MFMA phases carry no load-issue work.
+  const TileLoader<D, 4> loader(wave & 3);
+  if (grp == 1) loader.load_k(Kb, 0, N, kbuf0);
+
+  const int qrow = qt * BM + wave * 32 + li;
+  u32x4 qf[G::KS];
+  if (qrow < N) {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(Q + hoff + (size_t)qrow * D + 8 * hh);
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) qf[ks] = qp[2 * ks];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) qf[ks] = (u32x4){0u, 0u, 0u, 0u};
+  }
+  f32x16 acc[G::DB];
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
+  float m = -INFINITY, l = 0.f;
+  f32x16 sc[2];
+  u32x4 pb[2][2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) pb[sb][hq] = (u32x4){0u, 0u, 0u, 0u};
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // --- phases -----------------------------------------------------------
+  // Loads of slot 2t: K_{t+1} -> kbuf[(t+1)&1], V_t -> vbuf[t&1].  Issued
+  // unconditionally: for a tile past the end the descriptor size is 0, the
+  // loads fetch nothing and write zeros into a buffer no one reads again.
+  auto loads = [&](int t) {
+    loader.load_k(Kb, (t + 1) * G::BN, N, (t & 1) ? kbuf0 : kbuf1);
+    loader.load_v(Vb, t * G::BN, N, (t & 1) ? vbuf1 : vbuf0);
+  };
+  auto wait_loads = [] { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // MFMA phase of tile t: reads K_t from kbuf[t & 1] and (t >= 1) V_{t-1}
+  // from vbuf[(t - 1) & 1]; the buffer choice is a uniform offset.
+  const LdsLanes<D> ln;
+  auto mfma_tile = [&](int t) {
+    const lds_u8* kb = kbuf0 + (t & 1) * G::TILEB;
+    const lds_u8* vb = vbuf0 + ((t - 1) & 1) * G::TILEB;
+    mfma_phase<E, D>(kb, vb, ln, t > 0, pb, acc, qf, sc);
+  };
+  // VALU phase of tile t.
+  auto valu_full = [&] {
+    maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
+    l += softmax16<E, false>(sc, m, c2, pb, 0, N);
+  };
+  auto valu_any = [&](int t) {
+    const int j0 = t * G::BN;
+    if (j0 + G::BN > N) {
+      mask_tail16(sc, j0, N, c2);
+      maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
+      l += softmax16<E, true>(sc, m, c2, pb, j0, N);
+    } else {
+      valu_full();
+    }
+  };
+  auto pv_last = [&] {
+    const lds_u8* vb = vbuf0 + ((T - 1) & 1) * G::TILEB;
+    const uint32_t vq = ln.vq;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+      const lds_u8* va = vb + (vq ^ (uint32_t)(db << 6));
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+          const lds_u8* a0 = va + (32 * sb + 16 * hq) * G::ROWB;
+          const u32x2 lo = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
+          const u32x2 hi = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * G::ROWB)));
+          acc[db] = E::mfma((u32x4){lo[0], lo[1], hi[0], hi[1]}, pb[sb][hq], acc[db]);
+        }
+    }
+  };
+
+  // --- the two schedules: 2T + 2 barriers each ----------------------------
+  // One loop body per group over the full tiles 1 .. T-2; tile 0 and the
+  // last tile (which may be partial) are peeled.
+  if (grp == 0) {
+    // slot 2t: MFMA phase of tile t; slot 2t+1: VALU phase of tile t.
+    block_barrier(); mfma_tile(0);
+    block_barrier(); valu_any(0);
+    for (int t = 1; t < T - 1; ++t) {
+      block_barrier(); mfma_tile(t);
+      block_barrier(); valu_full();
+    }
+    if (T > 1) {
+      block_barrier(); mfma_tile(T - 1);
+      block_barrier(); valu_any(T - 1);
+    }
+    block_barrier(); pv_last();  // slot 2T
+    block_barrier();             // slot 2T + 1
+  } else {
+    // one slot behind: slot 2t+1: MFMA phase of tile t; slot 2t+2: VALU.
+    block_barrier(); loads(0);                        // slot 0
+    block_barrier(); mfma_tile(0); wait_loads();      // slot 1
+    block_barrier(); loads(1); valu_any(0);           // slot 2
+    for (int t = 1; t < T - 1; ++t) {
+      block_barrier(); mfma_tile(t); wait_loads();
+      block_barrier(); loads(t + 1); valu_full();
+    }
+    if (T > 1) {
+      block_barrier(); mfma_tile(T - 1); wait_loads();
+      block_barrier(); loads(T); valu_any(T - 1);
+    }
+    block_barrier(); pv_last();  // slot 2T + 1
+  }
+
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
   if (qrow < N) {
@@ -704,12 +994,40 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 template <class T>
 int launch(void (*kernel)(const T*, const T*, const T*, T*, float*, int, int, float),
-           int64_t nblocks, hipStream_t stream, const void* q, const void* k, const void* v,
-           void* o, float* lse, int N, int nqt, float c2) {
-  hipLaunchKernelGGL(kernel, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+           int64_t nblocks, int threads, hipStream_t stream, const void* q, const void* k,
+           const void* v, void* o, float* lse, int N, int nqt, float c2) {
+  hipLaunchKernelGGL(kernel, dim3((unsigned)nblocks), dim3(threads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k),
                      static_cast<const T*>(v), static_cast<T*>(o), lse, N, nqt, c2);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+constexpr int kNumCUs = 256;  // MI355X
+
+// Kernel choice for the 16-bit types: the 8-wave ping-pong kernel (256 query
+// rows per block) when it still gives every CU a block, else the 4-wave
+// pipelined kernel (128 rows per block, up to two blocks per CU).  The
+// environment variable ATTN_FWD_KERNEL=pingpong|pipelined forces one (for
+// tests and sweeps).
+bool use_pingpong(int64_t bh, int64_t N) {
+  const char* env = getenv("ATTN_FWD_KERNEL");
+  if (env != nullptr && strcmp(env, "pingpong") == 0) return true;
+  if (env != nullptr && strcmp(env, "pipelined") == 0) return false;
+  return bh * ((N + 255) / 256) >= kNumCUs;
+}
+
+template <class E, class T>
+int launch16(int64_t bh, int64_t N, int64_t d, hipStream_t s, const void* q, const void* k,
+             const void* v, void* o, float* lse, float c2) {
+  if (use_pingpong(bh, N)) {
+    const int64_t nqt = (N + 255) / 256;
+    if (bh * nqt > INT32_MAX) return ATTN_ERR_SHAPE;
+    auto kern = d == 128 ? attn_fwd_pp16<E, 128> : attn_fwd_pp16<E, 64>;
+    return launch<T>(kern, bh * nqt, kPPThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2);
+  }
+  const int64_t nqt = (N + 127) / 128;
+  auto kern = d == 128 ? attn_fwd_mfma16<E, 128> : attn_fwd_mfma16<E, 64>;
+  return launch<T>(kern, bh * nqt, kThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2);
 }
 
 }  // namespace
@@ -731,9 +1049,8 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULLPTR;
   const size_t esize = dtype == ATTN_DTYPE_F32 ? 4 : 2;
   if (elems > INT64_MAX / (int64_t)esize) return ATTN_ERR_SHAPE;
-  const int64_t nqt = (N + 127) / 128;  // BM = 128 for every instance
-  int64_t nblocks = 0;
-  if (!mul_ok(bh, nqt, &nblocks) || nblocks > INT32_MAX) return ATTN_ERR_SHAPE;
+  int64_t nblocks = 0;  // the largest grid: 128 query rows per block
+  if (!mul_ok(bh, (N + 127) / 128, &nblocks) || nblocks > INT32_MAX) return ATTN_ERR_SHAPE;
   auto misaligned = [](const void* p, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
   };
@@ -751,17 +1068,11 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   // --- launch -------------------------------------------------------------
   const float c2 = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int n = (int)N, nq = (int)nqt;
-  if (dtype == ATTN_DTYPE_BF16) {
-    if (d == 128) return launch(attn_fwd_mfma16<Bf16T, 128>, nblocks, s, q, k, v, o, lse, n, nq, c2);
-    return launch(attn_fwd_mfma16<Bf16T, 64>, nblocks, s, q, k, v, o, lse, n, nq, c2);
-  }
-  if (dtype == ATTN_DTYPE_F16) {
-    if (d == 128) return launch(attn_fwd_mfma16<F16T, 128>, nblocks, s, q, k, v, o, lse, n, nq, c2);
-    return launch(attn_fwd_mfma16<F16T, 64>, nblocks, s, q, k, v, o, lse, n, nq, c2);
-  }
-  if (d == 128) return launch(attn_fwd_mfma32<128>, nblocks, s, q, k, v, o, lse, n, nq, c2);
-  return launch(attn_fwd_mfma32<64>, nblocks, s, q, k, v, o, lse, n, nq, c2);
+  if (dtype == ATTN_DTYPE_BF16) return launch16<Bf16T, uint16_t>(bh, N, d, s, q, k, v, o, lse, c2);
+  if (dtype == ATTN_DTYPE_F16) return launch16<F16T, uint16_t>(bh, N, d, s, q, k, v, o, lse, c2);
+  const int64_t nqt = (N + 127) / 128;
+  auto kern = d == 128 ? attn_fwd_mfma32<128> : attn_fwd_mfma32<64>;
+  return launch<float>(kern, bh * nqt, kThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2);
 }
 
 extern "C" const char* attn_strerror(int code) {

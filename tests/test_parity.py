@@ -224,3 +224,25 @@ def test_binding_rejects_bad_arguments():
         attn.fwd(q.transpose(2, 3), q.transpose(2, 3), q.transpose(2, 3))
     with pytest.raises(ValueError):
         attn.attn_fwd(q, q, q, q, None, 0.125)  # output aliases an input
+
+
+# ---------------------------------------------------------------------------
+# both 16-bit kernels (8-wave ping-pong and 4-wave pipelined), forced
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("dtype,d,N,BH", [("bf16", 128, 1000, (1, 3)), ("f16", 64, 777, (2, 2)),
+                                          ("bf16", 64, 64, (1, 2)), ("f16", 128, 129, (1, 1)),
+                                          ("bf16", 128, 1, (2, 1)), ("bf16", 64, 4096, (1, 2)),
+                                          ("f16", 128, 2048, (2, 1))])
+def test_forced_kernel(kernel, dtype, d, N, BH, monkeypatch):
+    monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
+    q, k, v = datagen.make_qkv(BH[0], BH[1], N, d, dtype, seed=N + d)
+    full_parity(q, k, v, 1.0 / math.sqrt(d), dtype, f"{kernel} {dtype} d={d} N={N}")
+
+
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+def test_forced_kernel_hot_keys(kernel, monkeypatch):
+    monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
+    q, k, v = datagen.make_qkv(1, 2, 3000, 128, "bf16", seed=56, hot_frac=0.01, hot_mult=8.0)
+    full_parity(q, k, v, 1.0 / math.sqrt(128), "bf16", f"{kernel} hot keys")

@@ -535,14 +535,16 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
 // --- MFMA phase with lean registers ---------------------------------------
 //
-// acc += P V (from vb) followed by S^T = K Q^T (from kb), for the ping-pong
-// kernel.  LDS addresses: with the XOR swizzles above, the address of K
-// fragment (sb, ks) is (kq ^ (ks << 5)) + sb * 32 * ROWB and that of V^T
-// fragment (sb, hq, db, half) is (vq ^ (db << 6)) + (32 sb + 16 hq + 8 half)
-// * ROWB, with kq, vq per-lane constants (the XORed bits of kq / vq are the
-// swizzle bits, the row parts are multiples of ROWB), so each needs one base
-// register and one v_xor per ks / db instead of a register per fragment.
-// The LDS reads are scheduled a fixed LA MFMAs ahead of their use.
+// acc += P V (from the V tile at LDS offset vbo) followed by S^T = K Q^T (from
+// the K tile at kbo), for the ping-pong kernel.  LDS addresses: with the XOR
+// swizzles above, the address of K fragment (sb, ks) is
+// ((kq + kbo) ^ (ks << 5)) + sb * 32 * ROWB and that of V^T fragment
+// (sb, hq, db, half) is ((vq + vbo) ^ (db << 6)) + (32 sb + 16 hq + 8 half) *
+// ROWB, with kq, vq per-lane constants whose XORed bits are the swizzle bits
+// (row parts are multiples of ROWB) and kbo, vbo multiples of the tile size,
+// which leave those bits alone; so each fragment costs one v_xor and an
+// immediate offset.  The LDS reads are scheduled a fixed LA MFMAs ahead of
+// their use.
 template <int D>
 struct LdsLanes {
   uint32_t kq, vq;
@@ -557,9 +559,33 @@ struct LdsLanes {
   }
 };
 
+// acc += P V over one 64-key V tile (LDS byte offset vbo).
 template <class E, int D>
-__device__ __forceinline__ void mfma_phase(const lds_u8* kb, const lds_u8* vb, LdsLanes<D> ln,
-                                           bool with_pv, const u32x4 (&pb)[2][2],
+__device__ __forceinline__ void pv_tile(const lds_u8* lsm, uint32_t vq, uint32_t vbo,
+                                        const u32x4 (&pb)[2][2], f32x16 (&acc)[Geo16<D>::DB]) {
+  constexpr int ROWB = Geo16<D>::ROWB;
+  const uint32_t vqb = vq + vbo;
+#pragma unroll
+  for (int db = 0; db < Geo16<D>::DB; ++db) {
+    const lds_u8* va = lsm + (vqb ^ (uint32_t)(db << 6));
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        const lds_u8* a0 = va + (32 * sb + 16 * hq) * ROWB;
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * ROWB)));
+        acc[db] = E::mfma((u32x4){lo[0], lo[1], hi[0], hi[1]}, pb[sb][hq], acc[db]);
+      }
+  }
+}
+
+template <class E, int D>
+__device__ __forceinline__ void mfma_phase(const lds_u8* lsm, uint32_t kbo, uint32_t vbo,
+                                           LdsLanes<D> ln, bool with_pv,
+                                           const u32x4 (&pb)[2][2],
                                            f32x16 (&acc)[Geo16<D>::DB],
                                            const u32x4 (&qf)[Geo16<D>::KS], f32x16 (&s)[2]) {
   using G = Geo16<D>;
@@ -568,31 +594,16 @@ __device__ __forceinline__ void mfma_phase(const lds_u8* kb, const lds_u8* vb, L
   // of the SIMD (in its VALU phase) also has instructions ready, the MFMAs,
   // each of which keeps the matrix pipe busy for many cycles, issue first.
   __builtin_amdgcn_s_setprio(3);
-  // Fresh copies each phase, so the per-fragment XORs stay inside the loop.
+  // Fresh copies each phase, so the per-fragment XORs stay inside the phase.
   uint32_t kq = ln.kq, vq = ln.vq;
   __asm__ volatile("" : "+v"(kq), "+v"(vq));
-  if (with_pv) {
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db) {
-      const lds_u8* va = vb + (vq ^ (uint32_t)(db << 6));
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
-          const lds_u8* a0 = va + (32 * sb + 16 * hq) * ROWB;
-          const u32x2 lo = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
-          const u32x2 hi = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * ROWB)));
-          acc[db] = E::mfma((u32x4){lo[0], lo[1], hi[0], hi[1]}, pb[sb][hq], acc[db]);
-        }
-    }
-  }
+  if (with_pv) pv_tile<E, D>(lsm, vq, vbo, pb, acc);
+  const uint32_t kqb = kq + kbo;
   s[0] = (f32x16){};
   s[1] = (f32x16){};
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
-    const lds_u8* ka = kb + (kq ^ (uint32_t)(ks << 5));
+    const lds_u8* ka = lsm + (kqb ^ (uint32_t)(ks << 5));
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const u32x4 a = *(const lds_u32x4*)(ka + sb * 32 * ROWB);
@@ -626,6 +637,43 @@ __device__ __forceinline__ void mfma_phase(const lds_u8* kb, const lds_u8* vb, L
   __builtin_amdgcn_s_setprio(0);
 }
 
+// Tile loads of the ping-pong kernel, issued by the four waves of one group.
+// One buffer descriptor per tile and tensor: its base is the tile's first row
+// and its size covers only the tile's rows below N, so the hardware range
+// check zero-fills rows past the end of the sequence.  Load u of issuing wave
+// w fills LDS block u * 4 + w (rows u * STEP_ROWS + r0, as in TileLoader); the
+// per-lane source offsets are loop invariants.
+template <int D>
+struct PPLoader {
+  using G = Geo16<D, 4>;
+  static constexpr int NW = 4;
+  static constexpr int LPW = G::LOADS_PER_WAVE;  // loads per wave per tensor and tile
+  static constexpr int STEP = NW * G::ROWS_PER_LOAD * G::ROWB;
+  uint32_t koff, voff;
+  int wave;
+
+  __device__ __forceinline__ explicit PPLoader(int w) : wave(w) {
+    const int lane = threadIdx.x & 63;
+    const int r0 = wave * G::ROWS_PER_LOAD + lane / G::CH;
+    const int p = lane % G::CH;
+    koff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_k<D>(r0)) << 4));
+    voff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_v<D>(r0)) << 4));
+  }
+  // Rows j0 .. j0+63 (j0 < N) of X into the tile at LDS byte address lds.
+  __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int j0, int N,
+                                       uint32_t lds) const {
+    const i32x4 rsrc = buffer_rsrc(Xb + (size_t)j0 * G::ROWB, (N - j0) * G::ROWB);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u)
+      lds_dma16(rsrc, off + (uint32_t)(u * STEP), lds + (uint32_t)((u * NW + wave) * G::LOADB));
+  }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // --- ping-pong kernel ----------------------------------------------------------
 //
 // 8 waves = 256 query rows per block, in two groups of 4 waves; waves w and
@@ -637,14 +685,27 @@ __device__ __forceinline__ void mfma_phase(const lds_u8* kb, const lds_u8* vb, L
 // work that the MFMA pipe cannot do, instead of both competing for the same
 // unit at the same time.
 //
-// Slot k (every wave passes the same barriers): the work item of group g is
-// i = k - g; for 0 <= i < 2T item i is phase (i % 2) of tile i / 2, item 2T
-// is the final P_{T-1} V_{T-1}.  At even slots k = 2t the waves of group 1
-// (then in their VALU phase) start the loads of K_{t+1} and V_t; they await
-// them at the end of slot 2t + 1, in time for the first reader in slot 2t + 2.  Buffer reuse: K_{t+1} and V_t
-// overwrite K_{t-1} and V_{t-2}, whose last readers (phase 0 of tile t-1)
-// finished in slot 2t - 1.
+// Slot k (every wave passes the same barriers): group 0 runs the MFMA phase
+// of tile k/2 at even k and its VALU phase at odd k; group 1 does the same one
+// slot later.  Slot 2T is group 0's final P_{T-1} V_{T-1}, slot 2T + 1 group
+// 1's.
+//
+// K and V tiles stream through four-deep LDS rings (tile t in ring slot
+// t % 4).  Each group loads one tensor, right after its MFMA phase, where the
+// wave's issue port has slack (the VALU phases are the longer ones):
+//   * group 0, after the MFMA phase of tile t (slot 2t), loads V_{t+2}, which
+//     overwrites V_{t-2}; it awaits V_t at the end of its VALU phase of tile
+//     t (slot 2t + 1), in time for the MFMA phase of tile t + 1;
+//   * group 1, after the MFMA phase of tile t (slot 2t + 1), loads K_{t+3},
+//     which overwrites K_{t-1}, and awaits K_{t+1} right away, in time for
+//     the MFMA phase of tile t + 1 at slot 2t + 2.
+// The overwritten tiles were last read by the MFMA phases of tile t - 1
+// (slots 2t - 2 and 2t - 1).  Each load has about four slots to arrive: the
+// query blocks of a head stream the same tiles at about the same time, and
+// the first of them to ask for a tile pays the full memory latency.  K_0..K_2
+// and V_0, V_1 are loaded before the first slot.
 constexpr int kPPThreads = 512;
+constexpr int kRing = 4;
 
 template <class E, int D>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -653,12 +714,11 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    float* __restrict__ LSE, int N, int nqt, float c2) {
   using G = Geo16<D, 8>;
   constexpr int BM = 256;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
-  lds_u8* const lsm = (lds_u8*)smem;
-  lds_u8* const kbuf0 = lsm;
-  lds_u8* const kbuf1 = lsm + G::TILEB;
-  lds_u8* const vbuf0 = lsm + 2 * G::TILEB;
-  lds_u8* const vbuf1 = lsm + 3 * G::TILEB;
+  constexpr uint32_t TB = G::TILEB;
+  constexpr uint32_t VRING = kRing * TB;  // the V ring follows the K ring
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kRing * G::TILEB];
+  const lds_u8* const lsm = (const lds_u8*)smem;
+  const uint32_t lbase = lds_addr(lsm);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -672,10 +732,33 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
 
   const int T = (N + G::BN - 1) / G::BN;
-  // Only the waves of group 1 issue tile loads: they are in their VALU phase
-  // at every even slot, so the MFMA phases carry no load-issue work.
-  const TileLoader<D, 4> loader(wave & 3);
-  if (grp == 1) loader.load_k(Kb, 0, N, kbuf0);
+  // Group 0 loads V tiles, group 1 K tiles; all values here are wave-uniform.
+  const PPLoader<D> loader(wave & 3);
+  constexpr int LPW = PPLoader<D>::LPW;
+  const unsigned char* const Xb = grp == 0 ? Vb : Kb;
+  const uint32_t xoff = grp == 0 ? loader.voff : loader.koff;
+  const uint32_t xring = lbase + (grp == 0 ? VRING : 0u);
+  auto load_tile = [&](int j) {  // tile j of this group's tensor, into ring slot j % 4
+    loader.load(Xb, xoff, j * G::BN, N, xring + (uint32_t)(j % kRing) * TB);
+  };
+  // Wait until at most the loads of tiles j+1 and j+2 (those that exist) are
+  // still in flight, i.e. until tile j has landed (loads complete in order).
+  auto wait_tile = [&](int j) {
+    if (j + 2 < T)
+      wait_vmcnt<2 * LPW>();
+    else if (j + 1 < T)
+      wait_vmcnt<LPW>();
+    else
+      wait_vmcnt<0>();
+  };
+  if (grp == 0) {
+    load_tile(0);
+    if (T > 1) load_tile(1);
+  } else {
+    load_tile(0);
+    if (T > 1) load_tile(1);
+    if (T > 2) load_tile(2);
+  }
 
   const int qrow = qt * BM + wave * 32 + li;
   u32x4 qf[G::KS];
@@ -697,24 +780,23 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) pb[sb][hq] = (u32x4){0u, 0u, 0u, 0u};
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmcnt<0>();
+  // The compiler cannot see the DMA loads (inline asm) and would otherwise
+  // place its own waits for the Q loads at their first use, inside an MFMA
+  // phase, counting only the loads it knows of: with tile loads in flight
+  // those waits would stall on them.  Using Q here retires its loads in the
+  // compiler's bookkeeping before any tile load is issued.
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) __asm__ volatile("" ::"v"(qf[ks]));
 
   // --- phases -----------------------------------------------------------
-  // Loads of slot 2t: K_{t+1} -> kbuf[(t+1)&1], V_t -> vbuf[t&1].  Issued
-  // unconditionally: for a tile past the end the descriptor size is 0, the
-  // loads fetch nothing and write zeros into a buffer no one reads again.
-  auto loads = [&](int t) {
-    loader.load_k(Kb, (t + 1) * G::BN, N, (t & 1) ? kbuf0 : kbuf1);
-    loader.load_v(Vb, t * G::BN, N, (t & 1) ? vbuf1 : vbuf0);
-  };
-  auto wait_loads = [] { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  // MFMA phase of tile t: reads K_t from kbuf[t & 1] and (t >= 1) V_{t-1}
-  // from vbuf[(t - 1) & 1]; the buffer choice is a uniform offset.
+  // MFMA phase of tile t: reads K_t from K ring slot t % 4 and, for t >= 1,
+  // V_{t-1} from V ring slot (t - 1) % 4.
   const LdsLanes<D> ln;
   auto mfma_tile = [&](int t) {
-    const lds_u8* kb = kbuf0 + (t & 1) * G::TILEB;
-    const lds_u8* vb = vbuf0 + ((t - 1) & 1) * G::TILEB;
-    mfma_phase<E, D>(kb, vb, ln, t > 0, pb, acc, qf, sc);
+    const uint32_t kbo = (uint32_t)(t % kRing) * TB;
+    const uint32_t vbo = VRING + (uint32_t)((t + kRing - 1) % kRing) * TB;
+    mfma_phase<E, D>(lsm, kbo, vbo, ln, t > 0, pb, acc, qf, sc);
   };
   // VALU phase of tile t.
   auto valu_full = [&] {
@@ -732,54 +814,42 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
   };
   auto pv_last = [&] {
-    const lds_u8* vb = vbuf0 + ((T - 1) & 1) * G::TILEB;
-    const uint32_t vq = ln.vq;
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db) {
-      const lds_u8* va = vb + (vq ^ (uint32_t)(db << 6));
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
-          const lds_u8* a0 = va + (32 * sb + 16 * hq) * G::ROWB;
-          const u32x2 lo = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
-          const u32x2 hi = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * G::ROWB)));
-          acc[db] = E::mfma((u32x4){lo[0], lo[1], hi[0], hi[1]}, pb[sb][hq], acc[db]);
-        }
-    }
+    uint32_t vq = ln.vq;
+    __asm__ volatile("" : "+v"(vq));
+    pv_tile<E, D>(lsm, vq, VRING + (uint32_t)((T - 1) % kRing) * TB, pb, acc);
   };
 
   // --- the two schedules: 2T + 2 barriers each ----------------------------
   // One loop body per group over the full tiles 1 .. T-2; tile 0 and the
   // last tile (which may be partial) are peeled.
   if (grp == 0) {
-    // slot 2t: MFMA phase of tile t; slot 2t+1: VALU phase of tile t.
-    block_barrier(); mfma_tile(0);
-    block_barrier(); valu_any(0);
+    // slot 2t: MFMA phase of tile t, load V_{t+2}; slot 2t+1: VALU phase of
+    // tile t, await V_t.
+    block_barrier(); mfma_tile(0); if (2 < T) load_tile(2);
+    block_barrier(); valu_any(0); wait_tile(0);
     for (int t = 1; t < T - 1; ++t) {
-      block_barrier(); mfma_tile(t);
-      block_barrier(); valu_full();
+      block_barrier(); mfma_tile(t); if (t + 2 < T) load_tile(t + 2);
+      block_barrier(); valu_full(); wait_tile(t);
     }
     if (T > 1) {
       block_barrier(); mfma_tile(T - 1);
-      block_barrier(); valu_any(T - 1);
+      block_barrier(); valu_any(T - 1); wait_tile(T - 1);
     }
     block_barrier(); pv_last();  // slot 2T
     block_barrier();             // slot 2T + 1
   } else {
-    // one slot behind: slot 2t+1: MFMA phase of tile t; slot 2t+2: VALU.
-    block_barrier(); loads(0);                        // slot 0
-    block_barrier(); mfma_tile(0); wait_loads();      // slot 1
-    block_barrier(); loads(1); valu_any(0);           // slot 2
+    // one slot behind: slot 2t+1: MFMA phase of tile t, load K_{t+3}, await
+    // K_{t+1}; slot 2t+2: VALU phase of tile t.
+    block_barrier();  // slot 0
+    block_barrier(); mfma_tile(0); if (3 < T) load_tile(3); wait_tile(1);
+    block_barrier(); valu_any(0);
     for (int t = 1; t < T - 1; ++t) {
-      block_barrier(); mfma_tile(t); wait_loads();
-      block_barrier(); loads(t + 1); valu_full();
+      block_barrier(); mfma_tile(t); if (t + 3 < T) load_tile(t + 3); wait_tile(t + 1);
+      block_barrier(); valu_full();
     }
     if (T > 1) {
-      block_barrier(); mfma_tile(T - 1); wait_loads();
-      block_barrier(); loads(T); valu_any(T - 1);
+      block_barrier(); mfma_tile(T - 1); wait_tile(T);
+      block_barrier(); valu_any(T - 1);
     }
     block_barrier(); pv_last();  // slot 2T + 1
   }

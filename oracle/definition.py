@@ -17,6 +17,15 @@ What it computes, per batch b, head h and query row i, for keys j < N:
    (page 3 section 5: the kernel also stores the log-sum-exp of the scaled
    scores, max plus log of the exp-sum.)
 
+Causal variant (``causal=True``): query row i sees only keys j <= i.  Page 1
+section 4 notes that real kernels add a causal mask; page 3 section 3's
+decoder layer fills masked scores with -1e9 before the softmax, and page 3
+section 5's autograd wrapper passes a ``causal`` flag to the forward.  Here the
+masked scores are excluded outright (set to -inf, so their exponentials are
+exactly zero); with -1e9 they would underflow to zero in float64 anyway for
+any finite scores of moderate size.  Every row keeps at least key 0, so m_i is
+finite.
+
 The full N x N score matrix is materialised, one chunk of query rows at a time
 so that memory stays bounded (a 256 x 65536 fp64 chunk is 128 MiB).  The matrix
 products and the elementwise exp/log are numpy library primitives; there is no
@@ -56,12 +65,16 @@ def scores(q, k, scale: float) -> np.ndarray:
     return float(scale) * (q @ k.T)
 
 
-def _rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+def _rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, rows=None):
     """Steps 1-6 for a block of query rows of one head.
 
     q [M, d], k [N, d], v [N, dv] (float64).  Returns (o [M, dv], lse [M]).
+    ``rows`` (causal only): the absolute query index of each of the M rows;
+    row r then sees keys j <= rows[r] only.
     """
     s = float(scale) * (q @ k.T)            # 1. scaled scores, [M, N]
+    if rows is not None:                    #    causal: drop keys after the query
+        s[np.arange(k.shape[0])[None, :] > np.asarray(rows)[:, None]] = -np.inf
     m = s.max(axis=1, keepdims=True)        # 2. row max
     p = np.exp(s - m)                       # 3. max-subtracted exponentials
     l = p.sum(axis=1, keepdims=True)        # 4. row sums
@@ -70,9 +83,11 @@ def _rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     return o, lse
 
 
-def softmax_probs(q, k, scale: float) -> np.ndarray:
+def softmax_probs(q, k, scale: float, causal: bool = False) -> np.ndarray:
     """The attention weights p_ij / l_i for one head (small shapes only)."""
     s = scores(q, k, scale)
+    if causal:
+        s[np.triu(np.ones(s.shape, dtype=bool), 1)] = -np.inf
     m = s.max(axis=1, keepdims=True)
     p = np.exp(s - m)
     return p / p.sum(axis=1, keepdims=True)
@@ -85,9 +100,11 @@ def _default_workers() -> int:
         return max(1, os.cpu_count() or 1)
 
 
-def attention(q, k, v, scale: float, *, workers: int | None = None,
+def attention(q, k, v, scale: float, *, causal: bool = False, workers: int | None = None,
               row_chunk: int = ROW_CHUNK):
     """O and lse for q, k, v of shape [B, H, N, d] (any float input dtype).
+
+    ``causal``: query row i attends keys 0..i only.
 
     Returns (o, lse): float64 arrays of shape [B, H, N, d] and [B, H, N].
     Work is split into (b, h, row-chunk) tasks on a thread pool with BLAS held
@@ -109,13 +126,18 @@ def attention(q, k, v, scale: float, *, workers: int | None = None,
     def run(task):
         b, h, i0 = task
         i1 = min(N, i0 + row_chunk)
-        o[b, h, i0:i1], lse[b, h, i0:i1] = _rows(q[b, h, i0:i1], k[b, h], v[b, h], scale)
+        if causal:
+            o[b, h, i0:i1], lse[b, h, i0:i1] = _rows(q[b, h, i0:i1], k[b, h], v[b, h], scale,
+                                                     np.arange(i0, i1))
+        else:
+            o[b, h, i0:i1], lse[b, h, i0:i1] = _rows(q[b, h, i0:i1], k[b, h], v[b, h], scale)
 
     _run_tasks(run, tasks, workers)
     return o, lse
 
 
-def attention_rows(q, k, v, scale: float, index, *, workers: int | None = None):
+def attention_rows(q, k, v, scale: float, index, *, causal: bool = False,
+                   workers: int | None = None):
     """O and lse for selected query rows only.
 
     ``index`` is an integer array of shape [R, 3] holding (b, h, i) triples.
@@ -141,7 +163,10 @@ def attention_rows(q, k, v, scale: float, index, *, workers: int | None = None):
     def run(task):
         b, h, rs = task
         rows = index[rs, 2]
-        o[rs], lse[rs] = _rows(q[b, h, rows], k[b, h], v[b, h], scale)
+        if causal:
+            o[rs], lse[rs] = _rows(q[b, h, rows], k[b, h], v[b, h], scale, rows)
+        else:
+            o[rs], lse[rs] = _rows(q[b, h, rows], k[b, h], v[b, h], scale)
 
     _run_tasks(run, tasks, workers)
     return o, lse

@@ -18,6 +18,10 @@ zero (page 1's initial values).  A final partial block simply holds fewer keys,
 which is what masking padded keys to -inf achieves (page 4's softmax kernel
 pads with -inf so that exp of a pad is zero).
 
+With ``causal=True`` the scores of keys after the query are -inf inside each
+block (page 1 section 4's causal mask), so a block wholly after a query row
+adds nothing to it: p = 0 and, with m already finite from key 0, alpha = 1.
+
 In exact arithmetic this equals the two-pass definition in ``definition``; the
 oracle tests use it only to pin that invariant, for several block sizes,
 including sizes that do not divide N.
@@ -27,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 
 
-def attention_online(q, k, v, scale: float, block_n: int):
+def attention_online(q, k, v, scale: float, block_n: int, causal: bool = False):
     """O, lse for q, k, v [B, H, N, d] via the blockwise online recurrence."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -46,6 +50,8 @@ def attention_online(q, k, v, scale: float, block_n: int):
             for j0 in range(0, N, block_n):
                 j1 = min(N, j0 + block_n)
                 s = float(scale) * (qh @ kh[j0:j1].T)
+                if causal:
+                    s[np.arange(j0, j1)[None, :] > np.arange(N)[:, None]] = -np.inf
                 m_new = np.maximum(m, s.max(axis=1))
                 p = np.exp(s - m_new[:, None])
                 alpha = np.exp(m - m_new)

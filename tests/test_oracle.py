@@ -385,3 +385,132 @@ def test_online_mistake_is_caught():
     o, lse = _attn(q, k, v, 0.6)
     o2, _ = _online_no_alpha_on_acc(q, k, v, 0.6, 64)
     assert not np.allclose(o, o2, rtol=1e-6, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# causal variant: query i attends keys 0..i (page 1 section 4's causal mask,
+# page 3 section 3's masked_fill before the softmax, page 3 section 5's
+# ``causal`` flag)
+# --------------------------------------------------------------------------
+
+def _attn_causal(q, k, v, scale):
+    return oracle.attention(q, k, v, scale, causal=True, workers=1)
+
+
+def cpin_brute_force(attn):
+    """Pure-Python textbook softmax over the keys j <= i only."""
+    for (N, d, seed) in [(1, 1, 30), (2, 4, 31), (5, 4, 32), (17, 8, 33), (17, 1, 34)]:
+        q, k, v = _rand(1, 2, N, d, seed)
+        o, lse = attn(q, k, v, 0.8)
+        for h in range(2):
+            Q, K, V = q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist()
+            for i in range(N):
+                ob, lb = _brute_row(Q[i], K[:i + 1], V[:i + 1], 0.8)
+                np.testing.assert_allclose(o[0, h, i], ob, rtol=1e-12, atol=1e-12)
+                assert abs(lse[0, h, i] - lb) <= 1e-12 * max(1.0, abs(lb))
+
+
+def cpin_prefix(attn):
+    """Row i equals the unmasked definition on the prefix K[:i+1], V[:i+1]."""
+    q, k, v = _rand(2, 2, 40, 8, 35)
+    o, lse = attn(q, k, v, 0.5)
+    for i in (0, 1, 7, 20, 39):
+        op, lp = _attn(q[:, :, :i + 1], k[:, :, :i + 1], v[:, :, :i + 1], 0.5)
+        np.testing.assert_allclose(o[:, :, i], op[:, :, i], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, i], lp[:, :, i], rtol=1e-13, atol=1e-13)
+
+
+def cpin_first_row(attn):
+    """Closed form: row 0 sees only key 0, so O = v_0 and lse = scale * q_0 . k_0."""
+    q, k, v = _rand(1, 3, 12, 6, 36)
+    o, lse = attn(q, k, v, 0.3)
+    np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[:, :, 0], 0.3 * np.einsum("bhc,bhc->bh", q[:, :, 0], k[:, :, 0]),
+                               rtol=1e-14, atol=1e-14)
+
+
+def cpin_sdpa(attn):
+    for (B, H, N, d, seed, scale) in [(2, 3, 33, 16, 37, 0.25), (1, 2, 70, 64, 38, 0.125)]:
+        q, k, v = _rand(B, H, N, d, seed)
+        o, lse = attn(q, k, v, scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale,
+                                                               is_causal=True)
+        s = scale * (tq @ tk.transpose(-1, -2))
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        np.testing.assert_allclose(o, ref.numpy(), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def cpin_weights(attn):
+    """With V = I the outputs are the weights: rows sum to one, zero above the diagonal."""
+    N = 23
+    q, k, _ = _rand(1, 1, N, 6, 39)
+    o, _ = attn(q, k, np.eye(N)[None, None], 0.9)
+    np.testing.assert_allclose(o.sum(axis=-1), 1.0, atol=1e-12)
+    assert np.all(o[0, 0][np.triu(np.ones((N, N), dtype=bool), 1)] == 0.0)
+    assert np.all(np.diag(o[0, 0]) > 0.0)
+    np.testing.assert_allclose(o[0, 0], oracle.softmax_probs(q[0, 0], k[0, 0], 0.9, causal=True),
+                               atol=1e-13)
+
+
+def cpin_online_matches(attn):
+    for (N, bn) in [(50, 1), (50, 7), (130, 64), (33, 33)]:
+        q, k, v = _rand(1, 2, N, 8, 140 + N + bn)
+        k[..., ::9, :] *= 8.0
+        o, lse = attn(q, k, v, 0.6)
+        o2, lse2 = attention_online(q, k, v, 0.6, bn, causal=True)
+        np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, lse2, rtol=1e-13, atol=1e-12)
+
+
+CAUSAL_PINS = [cpin_brute_force, cpin_prefix, cpin_first_row, cpin_sdpa, cpin_weights,
+               cpin_online_matches]
+
+
+@pytest.mark.parametrize("pin", CAUSAL_PINS, ids=lambda p: p.__name__)
+def test_causal_oracle_pin(pin):
+    pin(_attn_causal)
+
+
+def test_causal_attention_rows_matches_full():
+    q, k, v = _rand(2, 2, 90, 8, 40)
+    o, lse = oracle.attention(q, k, v, 0.5, causal=True, workers=1, row_chunk=32)
+    idx = np.array([[0, 0, 0], [1, 1, 89], [0, 1, 45], [1, 0, 3], [1, 0, 33]])
+    orow, lrow = oracle.attention_rows(q, k, v, 0.5, idx, causal=True, workers=2)
+    for r, (b, h, i) in enumerate(idx):
+        np.testing.assert_allclose(orow[r], o[b, h, i], rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(lrow[r], lse[b, h, i], rtol=1e-15, atol=1e-15)
+
+
+def _cmut(mask_fn):
+    """A copy of the row kernel whose causal mask is ``mask_fn(j, i) -> masked``."""
+    def rows_fn(q, k, v, scale, rows=None):
+        s = scale * (q @ k.T)
+        if rows is not None:
+            s[mask_fn(np.arange(k.shape[0])[None, :], np.asarray(rows)[:, None])] = -np.inf
+        m = s.max(1, keepdims=True); p = np.exp(s - m); l = p.sum(1, keepdims=True)
+        return (p @ v) / l, m[:, 0] + np.log(l[:, 0])
+    return rows_fn
+
+
+CAUSAL_MUTANTS = {
+    "no_mask": _cmut(lambda j, i: np.zeros(np.broadcast(j, i).shape, dtype=bool)),
+    "diagonal_masked": _cmut(lambda j, i: j >= i),
+    "transposed_mask": _cmut(lambda j, i: j < i),
+    "row_index_off_by_one": _cmut(lambda j, i: j > i + 1),
+    "row_index_shifted_down": _cmut(lambda j, i: j > i - 1 + (i == 0)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CAUSAL_MUTANTS))
+def test_causal_planted_mistakes_are_caught(name, monkeypatch):
+    monkeypatch.setattr(attention_mod, "_rows", CAUSAL_MUTANTS[name])
+    caught = []
+    for pin in CAUSAL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(_attn_causal)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no causal pin caught {name}"

@@ -8,6 +8,7 @@ GPU is present, calls raise.
 
     o, lse = fwd(q, k, v)                  # allocate outputs, scale = 1/sqrt(d)
     attn_fwd(q, k, v, o, lse, scale)       # caller-owned outputs, async launch
+    p = plan(q, k, v, o, lse, scale); p()  # checked once, then relaunched cheaply
 
 Tensors are ``[B, H, N, d]`` contiguous, fp32/fp16/bf16, d in {64, 128};
 ``lse`` is ``[B, H, N]`` fp32 (or None).  Argument errors raise ValueError,
@@ -22,7 +23,8 @@ import os
 
 from .build import LIB
 
-__all__ = ["attn_fwd", "fwd", "attn_strerror", "attn_version", "library_path", "AttnError"]
+__all__ = ["attn_fwd", "fwd", "plan", "Plan", "attn_strerror", "attn_version", "library_path",
+           "AttnError"]
 
 ATTN_OK = 0
 ATTN_ERR_HIP = -8
@@ -113,28 +115,63 @@ def _check(q, k, v, o, lse):
     return codes[q.dtype]
 
 
+def _raise_for(rc: int) -> None:
+    if rc == ATTN_ERR_HIP:
+        raise RuntimeError(f"attn_fwd: {attn_strerror(rc)}")
+    if rc != ATTN_OK:
+        raise AttnError(rc, attn_strerror(rc))
+
+
+class Plan:
+    """One checked ``attn_fwd`` call whose arguments are marshalled once.
+
+    The tensors are validated when the plan is made; each call then only
+    passes the stored pointers, sizes and stream to the library (which still
+    validates them), so repeated launches cost little host time.  The caller
+    keeps the tensors alive and unchanged in shape while the plan is used.
+    """
+
+    def __init__(self, q, k, v, o, lse, scale: float, stream=None):
+        torch = _torch()
+        code_dtype = _check(q, k, v, o, lse)
+        B, H, N, d = (int(x) for x in q.shape)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        elif hasattr(stream, "cuda_stream"):
+            stream = stream.cuda_stream
+        self.device = q.device
+        self._fn = _load().attn_fwd
+        self._args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                      ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+                      ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                      B, H, N, d, float(scale), code_dtype, ctypes.c_void_p(stream))
+        self._tensors = (q, k, v, o, lse)  # keep the storage alive
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != ATTN_OK:
+            _raise_for(rc)
+
+
+def plan(q, k, v, o, lse, scale: float, stream=None) -> Plan:
+    """Check the arguments of ``attn_fwd`` once and return a relaunchable call.
+
+    q's device must be the current device whenever the plan is called."""
+    return Plan(q, k, v, o, lse, scale, stream)
+
+
 def attn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
     """O = softmax(scale * Q K^T) V into ``o`` (and the log-sum-exp into ``lse``).
 
     Asynchronous on ``stream`` (default: torch's current stream of q's device).
     """
     torch = _torch()
-    code_dtype = _check(q, k, v, o, lse)
-    B, H, N, d = (int(x) for x in q.shape)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
-    lib = _load()
-    with torch.cuda.device(q.device):
-        rc = lib.attn_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
-                          ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
-                          ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
-                          B, H, N, d, float(scale), code_dtype, ctypes.c_void_p(stream))
-    if rc == ATTN_ERR_HIP:
-        raise RuntimeError(f"attn_fwd: {attn_strerror(rc)}")
-    if rc != ATTN_OK:
-        raise AttnError(rc, attn_strerror(rc))
+    p = Plan(q, k, v, o, lse, scale, stream)
+    if torch.cuda.current_device() == p.device.index:
+        p()
+    else:
+        with torch.cuda.device(p.device):
+            p()
 
 
 def fwd(q, k, v, scale: float | None = None, return_lse: bool = True):

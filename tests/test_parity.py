@@ -234,7 +234,9 @@ def test_binding_rejects_bad_arguments():
 @pytest.mark.parametrize("dtype,d,N,BH", [("bf16", 128, 1000, (1, 3)), ("f16", 64, 777, (2, 2)),
                                           ("bf16", 64, 64, (1, 2)), ("f16", 128, 129, (1, 1)),
                                           ("bf16", 128, 1, (2, 1)), ("bf16", 64, 4096, (1, 2)),
-                                          ("f16", 128, 2048, (2, 1))])
+                                          ("f16", 128, 2048, (2, 1)), ("bf16", 128, 63, (1, 2)),
+                                          ("f16", 64, 65, (1, 2)), ("bf16", 64, 127, (2, 1)),
+                                          ("f16", 128, 257, (1, 2)), ("bf16", 128, 320, (1, 1))])
 def test_forced_kernel(kernel, dtype, d, N, BH, monkeypatch):
     monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
     q, k, v = datagen.make_qkv(BH[0], BH[1], N, d, dtype, seed=N + d)
@@ -246,3 +248,12 @@ def test_forced_kernel_hot_keys(kernel, monkeypatch):
     monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
     q, k, v = datagen.make_qkv(1, 2, 3000, 128, "bf16", seed=56, hot_frac=0.01, hot_mult=8.0)
     full_parity(q, k, v, 1.0 / math.sqrt(128), "bf16", f"{kernel} hot keys")
+
+
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 1.5])
+def test_forced_kernel_scales(kernel, scale, monkeypatch):
+    """Negative, zero and large scales on each 16-bit kernel."""
+    monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
+    q, k, v = datagen.make_qkv(1, 2, 700, 64, "bf16", seed=91)
+    full_parity(q, k, v, scale, "bf16", f"{kernel} scale {scale}")

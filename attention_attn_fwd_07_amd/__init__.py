@@ -10,10 +10,14 @@ GPU is present, calls raise.
     attn_fwd(q, k, v, o, lse, scale)       # caller-owned outputs, async launch
     p = plan(q, k, v, o, lse, scale); p()  # checked once, then relaunched cheaply
 
-Tensors are ``[B, H, N, d]`` contiguous, fp32/fp16/bf16, d in {64, 128};
-``lse`` is ``[B, H, N]`` fp32 (or None).  Argument errors raise ValueError,
-mirroring a wrapper that checks device, shape, dtype and contiguity before it
-launches anything (page 2 "Triton programming template", Python wrapper).
+Tensors are ``[B, H, N, d]`` fp32/fp16/bf16 with d in {64, 128}; the head
+dimension must be contiguous, the other three dimensions may have any strides
+that are multiples of 8 elements (so a ``[B, N, H, d]`` tensor viewed with
+``.transpose(1, 2)`` is accepted without a copy).  ``lse`` is ``[B, H, N]``
+fp32 contiguous (or None).  ``causal=True`` restricts query row i to keys
+0..i.  Argument errors raise ValueError, mirroring a wrapper that checks
+device, shape, dtype and layout before it launches anything (page 2 "Triton
+programming template", Python wrapper).
 """
 from __future__ import annotations
 
@@ -24,10 +28,24 @@ import os
 from .build import LIB
 
 __all__ = ["attn_fwd", "fwd", "plan", "Plan", "attn_strerror", "attn_version", "library_path",
-           "AttnError"]
+           "AttnError", "ATTN_CAUSAL"]
 
 ATTN_OK = 0
 ATTN_ERR_HIP = -8
+ATTN_CAUSAL = 1
+
+
+class _Args(ctypes.Structure):
+    """attn_fwd_args_t of include/attn_fwd.h."""
+
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+                ("flags", ctypes.c_uint),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+                ("stream", ctypes.c_void_p)]
 
 
 class AttnError(ValueError):
@@ -58,6 +76,8 @@ def _load():
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
                              ctypes.c_int, vp]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_ex.argtypes = [ctypes.POINTER(_Args)]
+    lib.attn_fwd_ex.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -94,8 +114,8 @@ def _check(q, k, v, o, lse):
             raise ValueError(f"{name} must be a GPU tensor")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D [B, H, N, d]")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+        if t.numel() > 0 and t.stride(3) != 1 and t.shape[3] > 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous")
     if not (q.shape == k.shape == v.shape == o.shape):
         raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} "
                          f"v{tuple(v.shape)} o{tuple(o.shape)}")
@@ -122,8 +142,15 @@ def _raise_for(rc: int) -> None:
         raise AttnError(rc, attn_strerror(rc))
 
 
+def _strides(t):
+    """(batch, head, row) element strides, or zeros for a contiguous tensor."""
+    if t.is_contiguous():
+        return (0, 0, 0)
+    return tuple(int(x) for x in t.stride()[:3])
+
+
 class Plan:
-    """One checked ``attn_fwd`` call whose arguments are marshalled once.
+    """One checked ``attn_fwd_ex`` call whose arguments are marshalled once.
 
     The tensors are validated when the plan is made; each call then only
     passes the stored pointers, sizes and stream to the library (which still
@@ -131,7 +158,7 @@ class Plan:
     keeps the tensors alive and unchanged in shape while the plan is used.
     """
 
-    def __init__(self, q, k, v, o, lse, scale: float, stream=None):
+    def __init__(self, q, k, v, o, lse, scale: float, stream=None, causal: bool = False):
         torch = _torch()
         code_dtype = _check(q, k, v, o, lse)
         B, H, N, d = (int(x) for x in q.shape)
@@ -140,33 +167,44 @@ class Plan:
         elif hasattr(stream, "cuda_stream"):
             stream = stream.cuda_stream
         self.device = q.device
-        self._fn = _load().attn_fwd
-        self._args = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
-                      ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
-                      ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
-                      B, H, N, d, float(scale), code_dtype, ctypes.c_void_p(stream))
+        self._fn = _load().attn_fwd_ex
+        a = _Args()
+        a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+        a.lse = lse.data_ptr() if lse is not None else None
+        a.B, a.H, a.N, a.d = B, H, N, d
+        a.scale = float(scale)
+        a.dtype = code_dtype
+        a.flags = ATTN_CAUSAL if causal else 0
+        a.q_stride[:] = _strides(q)
+        a.k_stride[:] = _strides(k)
+        a.v_stride[:] = _strides(v)
+        a.o_stride[:] = _strides(o)
+        a.stream = stream
+        self._args = a
+        self._ref = ctypes.byref(a)
         self._tensors = (q, k, v, o, lse)  # keep the storage alive
 
     def __call__(self) -> None:
-        rc = self._fn(*self._args)
+        rc = self._fn(self._ref)
         if rc != ATTN_OK:
             _raise_for(rc)
 
 
-def plan(q, k, v, o, lse, scale: float, stream=None) -> Plan:
-    """Check the arguments of ``attn_fwd`` once and return a relaunchable call.
+def plan(q, k, v, o, lse, scale: float, stream=None, causal: bool = False) -> Plan:
+    """Check the arguments of ``attn_fwd_ex`` once and return a relaunchable call.
 
     q's device must be the current device whenever the plan is called."""
-    return Plan(q, k, v, o, lse, scale, stream)
+    return Plan(q, k, v, o, lse, scale, stream, causal)
 
 
-def attn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
+def attn_fwd(q, k, v, o, lse, scale: float, stream=None, causal: bool = False) -> None:
     """O = softmax(scale * Q K^T) V into ``o`` (and the log-sum-exp into ``lse``).
 
     Asynchronous on ``stream`` (default: torch's current stream of q's device).
+    ``causal``: query row i attends keys 0..i only.
     """
     torch = _torch()
-    p = Plan(q, k, v, o, lse, scale, stream)
+    p = Plan(q, k, v, o, lse, scale, stream, causal)
     if torch.cuda.current_device() == p.device.index:
         p()
     else:
@@ -174,13 +212,15 @@ def attn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
             p()
 
 
-def fwd(q, k, v, scale: float | None = None, return_lse: bool = True):
-    """Allocate O (and lse) and run ``attn_fwd``; scale defaults to 1/sqrt(d)."""
+def fwd(q, k, v, scale: float | None = None, return_lse: bool = True, causal: bool = False):
+    """Allocate O (and lse) and run ``attn_fwd``; scale defaults to 1/sqrt(d).
+
+    O is allocated contiguous [B, H, N, d] whatever q's strides."""
     torch = _torch()
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = (torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
            if return_lse else None)
-    attn_fwd(q, k, v, o, lse, scale)
+    attn_fwd(q, k, v, o, lse, scale, causal=causal)
     return o, lse

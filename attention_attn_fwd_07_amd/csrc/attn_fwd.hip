@@ -64,6 +64,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kXcds = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kThreads = 256; // 4 wave64s per block
 
+// Where one head's rows live: element strides (batch, head, row) of Q, K, V
+// and O, the head dimension being contiguous, and H to split a block's
+// b * H + h index.  Contiguous [B, H, N, d] tensors have strides
+// {H N d, N d, d}.
+struct Layout {
+  int H;
+  long long q[3], k[3], v[3], o[3];
+  __device__ __forceinline__ long long base(const long long (&st)[3], int bh) const {
+    const int b = bh / H, h = bh - b * H;
+    return (long long)b * st[0] + (long long)h * st[1];
+  }
+};
+
 // ---------------------------------------------------------------------------
 // element traits for the 16-bit paths
 // ---------------------------------------------------------------------------
@@ -256,35 +269,37 @@ struct TileLoader {
   static constexpr int STEP_ROWS = NW * G::ROWS_PER_LOAD;  // rows between loads u, u+1
   static_assert(STEP_ROWS % 16 == 0, "swizzle bits must not depend on u");
   uint32_t koff, voff;  // this lane's byte offset from the group's first row
+  int krs, vrs;         // bytes between consecutive rows of K and of V in memory
   int wave;             // index of the issuing wave among the NWAVES, uniform
 
-  __device__ __forceinline__ explicit TileLoader(int w) : wave(w) {
+  __device__ __forceinline__ TileLoader(int w, int k_row_bytes, int v_row_bytes)
+      : krs(k_row_bytes), vrs(v_row_bytes), wave(w) {
     const int lane = threadIdx.x & 63;
     const int r0 = wave * G::ROWS_PER_LOAD + lane / G::CH;
     const int p = lane % G::CH;
-    koff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_k<D>(r0)) << 4));
-    voff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_v<D>(r0)) << 4));
+    koff = (uint32_t)(r0 * krs + ((p ^ swz_k<D>(r0)) << 4));
+    voff = (uint32_t)(r0 * vrs + ((p ^ swz_v<D>(r0)) << 4));
   }
 
-  // Rows j0 .. j0+63 of one tensor (K or V, with its lane offset) -> xb.
-  __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int j0, int N,
-                                       lds_u8* xb) const {
+  // Rows j0 .. j0+63 of one tensor (K or V, with its lane offset and row
+  // stride rs in bytes) -> xb, stored densely (ROWB bytes per row) in LDS.
+  __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int rs, int j0,
+                                       int N, lds_u8* xb) const {
 #pragma unroll
     for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
       const int row = j0 + u * STEP_ROWS;
-      const int bytes = N > row ? (N - row) * G::ROWB : 0;  // N*ROWB < 2^31
+      const int bytes = N > row ? (N - row) * rs : 0;  // N * rs < 2^31 (checked on the host)
       const int blk = u * NW + wave;
-      lds_dma16(buffer_rsrc(Xb + (size_t)row * G::ROWB, bytes), off,
-                lds_addr(xb + blk * G::LOADB));
+      lds_dma16(buffer_rsrc(Xb + (size_t)row * rs, bytes), off, lds_addr(xb + blk * G::LOADB));
     }
   }
   __device__ __forceinline__ void load_k(const unsigned char* Kb, int j0, int N,
                                          lds_u8* kb) const {
-    load(Kb, koff, j0, N, kb);
+    load(Kb, koff, krs, j0, N, kb);
   }
   __device__ __forceinline__ void load_v(const unsigned char* Vb, int j0, int N,
                                          lds_u8* vb) const {
-    load(Vb, voff, j0, N, vb);
+    load(Vb, voff, vrs, j0, N, vb);
   }
 };
 
@@ -313,16 +328,45 @@ __device__ __forceinline__ void qk16(const lds_u8* kb, const u32x4 (&qf)[Geo16<D
   }
 }
 
-// Keys >= N in the last, partial tile: a value that cannot win the row
-// extreme (the probabilities of these keys are zeroed in softmax16).
-__device__ __forceinline__ void mask_tail16(f32x16 (&s)[2], int j0, int N, float c2) {
+// The keys a query row may see: j <= lim with lim = N - 1, and for causal
+// attention also lim <= the row's own index (query i attends keys 0..i).
+// lane_lim is the lane's limit, wave_lim the smallest over the wave (uniform);
+// a key tile needs masking only if it reaches past wave_lim.
+template <bool CAUSAL>
+struct KeyLimit {
+  int lane_lim, wave_lim;
+  __device__ __forceinline__ KeyLimit(int N, int qrow, int qrow0) {
+    lane_lim = CAUSAL ? min(N - 1, qrow) : N - 1;
+    wave_lim = CAUSAL ? min(N - 1, qrow0) : N - 1;
+  }
+  __device__ __forceinline__ bool partial(int j0, int bn) const { return j0 + bn - 1 > wave_lim; }
+};
+
+// Number of key tiles of width bn that a block of query rows q0 .. q0+bm-1
+// visits: all of them, or for causal attention those up to its last row.
+template <bool CAUSAL>
+__device__ __forceinline__ int key_tiles(int N, int q0, int bm, int bn) {
+  const int nk = CAUSAL ? min(N, q0 + bm) : N;
+  return (nk + bn - 1) / bn;
+}
+
+// Query tile of a block: for causal attention the tiles of a head are taken
+// last first, so that the blocks with the most key tiles start first.
+template <bool CAUSAL>
+__device__ __forceinline__ int query_tile(int t, int nqt) {
+  return CAUSAL ? nqt - 1 - t : t;
+}
+
+// Keys past the lane's limit in a partial tile: a value that cannot win the
+// row extreme (the probabilities of these keys are zeroed in softmax16).
+__device__ __forceinline__ void mask_tail16(f32x16 (&s)[2], int j0, int lim, float c2) {
   const int hh = (threadIdx.x & 63) >> 5;
   const float neutral = c2 >= 0.f ? -INFINITY : INFINITY;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N) s[sb][r] = neutral;
+      if (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) > lim) s[sb][r] = neutral;
 }
 
 // Row max of the log2-scaled scores t = s * c2 over the tile (for c2 < 0 the
@@ -357,7 +401,7 @@ __device__ __forceinline__ void maybe_rescale(float m_tile, float& m, float& l,
 // log-sum-exp output depends on it directly, so it sums unrounded values).
 template <class E, bool TAIL>
 __device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float c2,
-                                           u32x4 (&pb)[2][2], int j0, int N) {
+                                           u32x4 (&pb)[2][2], int j0, int lim) {
   const int hh = (threadIdx.x & 63) >> 5;
   // Eight independent partial sums: a single running sum would be a chain
   // of 32 dependent adds, whose latency nothing hides when one wave of the
@@ -369,7 +413,7 @@ __device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       p[r] = fast_exp2(fmaf(s[sb][r], c2, -m));
-      if (TAIL && (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) >= N)) p[r] = 0.f;
+      if (TAIL && (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) > lim)) p[r] = 0.f;
       part[r & 7] += p[r];
     }
 #pragma unroll
@@ -423,11 +467,11 @@ __device__ __forceinline__ void pv16(const lds_u8* vb, const u32x4 (&pb)[2][2],
 // S_{t+1} and, rarely, rescales.  K therefore runs one tile ahead of V:
 // iteration t reads K_{t+1} and V_t while K_{t+2} and V_{t+1} stream into
 // the other K and V buffers.
-template <class E, int D>
+template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                     float* __restrict__ LSE, int N, int nqt, float c2) {
+                     float* __restrict__ LSE, int N, int nqt, float c2, Layout L) {
   using G = Geo16<D, 4>;
   constexpr int BM = 128;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
@@ -441,13 +485,15 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int li = lane & 31, hh = lane >> 5;
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / nqt, qt = tile - bh * nqt;
-  const size_t hoff = (size_t)bh * N * D;
-  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + hoff);
-  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
+  const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
+  const uint16_t* const Qh = Q + L.base(L.q, bh);
+  uint16_t* const Oh = O + L.base(L.o, bh);
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + L.base(L.k, bh));
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + L.base(L.v, bh));
 
-  const int ntiles = (N + G::BN - 1) / G::BN;
-  const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+  const int ntiles = key_tiles<CAUSAL>(N, qt * BM, BM, G::BN);
+  const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+                               (int)(L.k[2] * 2), (int)(L.v[2] * 2));
   loader.load_k(Kb, 0, N, kbuf0);
   loader.load_v(Vb, 0, N, vbuf0);
   if (ntiles > 1) loader.load_k(Kb, G::BN, N, kbuf1);
@@ -455,9 +501,10 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // Q fragment, resident for the whole key loop: lane (li, hh) holds
   // d = 16 ks + 8 hh + [0, 8) of query row qrow.
   const int qrow = qt * BM + wave * 32 + li;
+  const KeyLimit<CAUSAL> kl(N, qrow, qt * BM + wave * 32);
   u32x4 qf[G::KS];
   if (qrow < N) {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(Q + hoff + (size_t)qrow * D + 8 * hh);
+    const u32x4* qp = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * L.q[2] + 8 * hh);
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) qf[ks] = qp[2 * ks];
   } else {
@@ -474,7 +521,7 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   f32x16 sA[2], sB[2];
   qk16<E, D>(kbuf0, qf, sA);
-  if (G::BN > N) mask_tail16(sA, 0, N, c2);
+  if (kl.partial(0, G::BN)) mask_tail16(sA, 0, kl.lane_lim, c2);
   float m = tile_max16(sA, c2);  // the first tile sets the reference exactly
   block_barrier();               // kbuf0 is free for K_2 only after every wave read K_0
 
@@ -484,10 +531,13 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (t + 2 < ntiles) loader.load_k(Kb, j1 + G::BN, N, kb_load);
     loader.load_v(Vb, j1, N, vb_load);
     u32x4 pb[2][2];
-    l += softmax16<E, false>(cur, m, c2, pb, 0, N);  // tiles before the last are full
+    if (CAUSAL && kl.partial(t * G::BN, G::BN))  // a diagonal tile (others are full)
+      l += softmax16<E, true>(cur, m, c2, pb, t * G::BN, kl.lane_lim);
+    else
+      l += softmax16<E, false>(cur, m, c2, pb, 0, 0);
     qk16<E, D>(kb_next, qf, nxt);
     pv16<E, D>(vb_cur, pb, acc);
-    if (j1 + G::BN > N) mask_tail16(nxt, j1, N, c2);
+    if (kl.partial(j1, G::BN)) mask_tail16(nxt, j1, kl.lane_lim, c2);
     maybe_rescale<D>(tile_max16(nxt, c2), m, l, acc);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads landed
     block_barrier();                                     // ... and everyone's
@@ -495,10 +545,10 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   auto last = [&](int t, const f32x16 (&cur)[2], const lds_u8* vb_cur) {
     u32x4 pb[2][2];
     const int j0 = t * G::BN;
-    if (j0 + G::BN > N)
-      l += softmax16<E, true>(cur, m, c2, pb, j0, N);
+    if (kl.partial(j0, G::BN))
+      l += softmax16<E, true>(cur, m, c2, pb, j0, kl.lane_lim);
     else
-      l += softmax16<E, false>(cur, m, c2, pb, j0, N);
+      l += softmax16<E, false>(cur, m, c2, pb, j0, 0);
     pv16<E, D>(vb_cur, pb, acc);
   };
 
@@ -519,7 +569,7 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
   if (qrow < N) {
-    uint16_t* op = O + hoff + (size_t)qrow * D;
+    uint16_t* op = Oh + (size_t)qrow * L.o[2];
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -648,24 +698,28 @@ struct PPLoader {
   using G = Geo16<D, 4>;
   static constexpr int NW = 4;
   static constexpr int LPW = G::LOADS_PER_WAVE;  // loads per wave per tensor and tile
-  static constexpr int STEP = NW * G::ROWS_PER_LOAD * G::ROWB;
+  static constexpr int STEP_ROWS = NW * G::ROWS_PER_LOAD;  // rows between loads u, u+1
   uint32_t koff, voff;
+  int krs, vrs;  // bytes between consecutive rows of K and of V in memory
   int wave;
 
-  __device__ __forceinline__ explicit PPLoader(int w) : wave(w) {
+  __device__ __forceinline__ PPLoader(int w, int k_row_bytes, int v_row_bytes)
+      : krs(k_row_bytes), vrs(v_row_bytes), wave(w) {
     const int lane = threadIdx.x & 63;
     const int r0 = wave * G::ROWS_PER_LOAD + lane / G::CH;
     const int p = lane % G::CH;
-    koff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_k<D>(r0)) << 4));
-    voff = (uint32_t)(r0 * G::ROWB + ((p ^ swz_v<D>(r0)) << 4));
+    koff = (uint32_t)(r0 * krs + ((p ^ swz_k<D>(r0)) << 4));
+    voff = (uint32_t)(r0 * vrs + ((p ^ swz_v<D>(r0)) << 4));
   }
-  // Rows j0 .. j0+63 (j0 < N) of X into the tile at LDS byte address lds.
-  __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int j0, int N,
-                                       uint32_t lds) const {
-    const i32x4 rsrc = buffer_rsrc(Xb + (size_t)j0 * G::ROWB, (N - j0) * G::ROWB);
+  // Rows j0 .. j0+63 (j0 < N) of X (row stride rs bytes) into the tile at
+  // LDS byte address lds.
+  __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int rs, int j0,
+                                       int N, uint32_t lds) const {
+    const i32x4 rsrc = buffer_rsrc(Xb + (size_t)j0 * rs, (N - j0) * rs);
 #pragma unroll
     for (int u = 0; u < LPW; ++u)
-      lds_dma16(rsrc, off + (uint32_t)(u * STEP), lds + (uint32_t)((u * NW + wave) * G::LOADB));
+      lds_dma16(rsrc, off + (uint32_t)(u * STEP_ROWS * rs),
+                lds + (uint32_t)((u * NW + wave) * G::LOADB));
   }
 };
 
@@ -707,11 +761,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 constexpr int kPPThreads = 512;
 constexpr int kRing = 4;
 
-template <class E, int D>
+template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                   float* __restrict__ LSE, int N, int nqt, float c2) {
+                   float* __restrict__ LSE, int N, int nqt, float c2, Layout L) {
   using G = Geo16<D, 8>;
   constexpr int BM = 256;
   constexpr uint32_t TB = G::TILEB;
@@ -726,24 +780,26 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int li = lane & 31, hh = lane >> 5;
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / nqt, qt = tile - bh * nqt;
-  const size_t hoff = (size_t)bh * N * D;
-  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + hoff);
-  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
+  const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
+  const uint16_t* const Qh = Q + L.base(L.q, bh);
+  uint16_t* const Oh = O + L.base(L.o, bh);
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + L.base(L.k, bh));
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + L.base(L.v, bh));
 
-  const int T = (N + G::BN - 1) / G::BN;
+  const int T = key_tiles<CAUSAL>(N, qt * BM, BM, G::BN);
   // Group 0 loads V tiles, group 1 K tiles; all values here are wave-uniform.
-  const PPLoader<D> loader(wave & 3);
+  const PPLoader<D> loader(wave & 3, (int)(L.k[2] * 2), (int)(L.v[2] * 2));
   constexpr int LPW = PPLoader<D>::LPW;
   const unsigned char* const Xb = grp == 0 ? Vb : Kb;
   const uint32_t xoff = grp == 0 ? loader.voff : loader.koff;
+  const int xrs = grp == 0 ? loader.vrs : loader.krs;
   const uint32_t xring = lbase + (grp == 0 ? VRING : 0u);
-  auto load_tile = [&](int j) {  // tile j of this group's tensor, into ring slot j % 4
-    loader.load(Xb, xoff, j * G::BN, N, xring + (uint32_t)(j % kRing) * TB);
+  auto load_tile = [&](int j) __attribute__((always_inline)) {  // tile j of this group's tensor, into ring slot j % 4
+    loader.load(Xb, xoff, xrs, j * G::BN, N, xring + (uint32_t)(j % kRing) * TB);
   };
   // Wait until at most the loads of tiles j+1 and j+2 (those that exist) are
   // still in flight, i.e. until tile j has landed (loads complete in order).
-  auto wait_tile = [&](int j) {
+  auto wait_tile = [&](int j) __attribute__((always_inline)) {
     if (j + 2 < T)
       wait_vmcnt<2 * LPW>();
     else if (j + 1 < T)
@@ -761,9 +817,10 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 
   const int qrow = qt * BM + wave * 32 + li;
+  const KeyLimit<CAUSAL> kl(N, qrow, qt * BM + wave * 32);
   u32x4 qf[G::KS];
   if (qrow < N) {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(Q + hoff + (size_t)qrow * D + 8 * hh);
+    const u32x4* qp = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * L.q[2] + 8 * hh);
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) qf[ks] = qp[2 * ks];
   } else {
@@ -793,27 +850,35 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // MFMA phase of tile t: reads K_t from K ring slot t % 4 and, for t >= 1,
   // V_{t-1} from V ring slot (t - 1) % 4.
   const LdsLanes<D> ln;
-  auto mfma_tile = [&](int t) {
+  auto mfma_tile = [&](int t) __attribute__((always_inline)) {
     const uint32_t kbo = (uint32_t)(t % kRing) * TB;
     const uint32_t vbo = VRING + (uint32_t)((t + kRing - 1) % kRing) * TB;
     mfma_phase<E, D>(lsm, kbo, vbo, ln, t > 0, pb, acc, qf, sc);
   };
   // VALU phase of tile t.
-  auto valu_full = [&] {
+  auto valu_full = [&]() __attribute__((always_inline)) {
     maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
-    l += softmax16<E, false>(sc, m, c2, pb, 0, N);
+    l += softmax16<E, false>(sc, m, c2, pb, 0, 0);
   };
-  auto valu_any = [&](int t) {
+  auto valu_any = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * G::BN;
-    if (j0 + G::BN > N) {
-      mask_tail16(sc, j0, N, c2);
+    if (kl.partial(j0, G::BN)) {
+      mask_tail16(sc, j0, kl.lane_lim, c2);
       maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
-      l += softmax16<E, true>(sc, m, c2, pb, j0, N);
+      l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
     } else {
       valu_full();
     }
   };
-  auto pv_last = [&] {
+  // Tiles between the first and the last: all full without a causal mask;
+  // with one, the block's last tiles cross the diagonal.
+  auto valu_mid = [&](int t) __attribute__((always_inline)) {
+    if (CAUSAL)
+      valu_any(t);
+    else
+      valu_full();
+  };
+  auto pv_last = [&]() __attribute__((always_inline)) {
     uint32_t vq = ln.vq;
     __asm__ volatile("" : "+v"(vq));
     pv_tile<E, D>(lsm, vq, VRING + (uint32_t)((T - 1) % kRing) * TB, pb, acc);
@@ -829,7 +894,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     block_barrier(); valu_any(0); wait_tile(0);
     for (int t = 1; t < T - 1; ++t) {
       block_barrier(); mfma_tile(t); if (t + 2 < T) load_tile(t + 2);
-      block_barrier(); valu_full(); wait_tile(t);
+      block_barrier(); valu_mid(t); wait_tile(t);
     }
     if (T > 1) {
       block_barrier(); mfma_tile(T - 1);
@@ -845,7 +910,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     block_barrier(); valu_any(0);
     for (int t = 1; t < T - 1; ++t) {
       block_barrier(); mfma_tile(t); if (t + 3 < T) load_tile(t + 3); wait_tile(t + 1);
-      block_barrier(); valu_full();
+      block_barrier(); valu_mid(t);
     }
     if (T > 1) {
       block_barrier(); mfma_tile(T - 1); wait_tile(T);
@@ -857,7 +922,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
   if (qrow < N) {
-    uint16_t* op = O + hoff + (size_t)qrow * D;
+    uint16_t* op = Oh + (size_t)qrow * L.o[2];
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -896,10 +961,10 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c2) {
+    float* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c2, Layout L) {
   using G = Geo32<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM];
 
@@ -907,18 +972,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   const int li = lane & 31, hh = lane >> 5;
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / nqt, qt = tile - bh * nqt;
-  const size_t hoff = (size_t)bh * N * D;
-  const float* Qh = Q + hoff;
-  const float* Kh = K + hoff;
-  const float* Vh = V + hoff;
+  const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
+  const float* Qh = Q + L.base(L.q, bh);
+  const float* Kh = K + L.base(L.k, bh);
+  const float* Vh = V + L.base(L.v, bh);
+  float* const Oh = O + L.base(L.o, bh);
 
   // Contraction index of K*Q^T: lane half hh covers d in [hh*D/2, (hh+1)*D/2),
   // one d per MFMA k-step.
   const int qrow = qt * G::BM + wave * 32 + li;
+  const KeyLimit<CAUSAL> kl(N, qrow, qt * G::BM + wave * 32);
   float qf[G::QV];
   if (qrow < N) {
-    const f32x4* qp = reinterpret_cast<const f32x4*>(Qh + (size_t)qrow * D + hh * G::QV);
+    const f32x4* qp = reinterpret_cast<const f32x4*>(Qh + (size_t)qrow * L.q[2] + hh * G::QV);
 #pragma unroll
     for (int u = 0; u < G::QV / 4; ++u) {
       const f32x4 x = qp[u];
@@ -934,24 +1000,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
   float m = -INFINITY, l = 0.f;
 
-  const int ntiles = (N + G::BN - 1) / G::BN;
+  const int ntiles = key_tiles<CAUSAL>(N, qt * G::BM, G::BM, G::BN);
   f32x4 kr[G::CPT], vr[G::CPT];
-  auto gload = [&](int j0) {
+  auto gload = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < G::CPT; ++u) {
       const int ci = threadIdx.x + u * kThreads;
       const int row = ci / G::CH, c = ci % G::CH;
       if (j0 + row < N) {
-        const size_t off = (size_t)(j0 + row) * D + c * 4;
-        kr[u] = *reinterpret_cast<const f32x4*>(Kh + off);
-        vr[u] = *reinterpret_cast<const f32x4*>(Vh + off);
+        kr[u] = *reinterpret_cast<const f32x4*>(Kh + (size_t)(j0 + row) * L.k[2] + c * 4);
+        vr[u] = *reinterpret_cast<const f32x4*>(Vh + (size_t)(j0 + row) * L.v[2] + c * 4);
       } else {
         kr[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
         vr[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
       }
     }
   };
-  auto swrite = [&](unsigned char* kb, unsigned char* vb) {
+  auto swrite = [&](unsigned char* kb, unsigned char* vb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < G::CPT; ++u) {
       const int ci = threadIdx.x + u * kThreads;
@@ -987,12 +1052,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
         s = mfma_f32(a[3], qf[4 * u + 3], s);
       }
     }
-    const bool tail = j0 + G::BN > N;
+    const bool tail = kl.partial(j0, G::BN);
     if (tail) {
       const float neutral = c2 >= 0.f ? -INFINITY : INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (j0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= N) s[r] = neutral;
+        if (j0 + 8 * (r >> 2) + 4 * hh + (r & 3) > kl.lane_lim) s[r] = neutral;
     }
     const float mt = c2 >= 0.f ? xhalf_max(frag_max(s)) : xhalf_min(frag_min(s));
     const float m_new = fmaxf(m, mt * c2);
@@ -1002,7 +1067,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p = fast_exp2(fmaf(s[r], c2, -m_new));
-      if (tail && (j0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= N)) p = 0.f;
+      if (tail && (j0 + 8 * (r >> 2) + 4 * hh + (r & 3) > kl.lane_lim)) p = 0.f;
       s[r] = p;
       rs += p;
     }
@@ -1034,7 +1099,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
   if (qrow < N) {
-    float* op = O + hoff + (size_t)qrow * D;
+    float* op = Oh + (size_t)qrow * L.o[2];
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -1063,12 +1128,12 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 }
 
 template <class T>
-int launch(void (*kernel)(const T*, const T*, const T*, T*, float*, int, int, float),
+int launch(void (*kernel)(const T*, const T*, const T*, T*, float*, int, int, float, Layout),
            int64_t nblocks, int threads, hipStream_t stream, const void* q, const void* k,
-           const void* v, void* o, float* lse, int N, int nqt, float c2) {
+           const void* v, void* o, float* lse, int N, int nqt, float c2, const Layout& L) {
   hipLaunchKernelGGL(kernel, dim3((unsigned)nblocks), dim3(threads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k),
-                     static_cast<const T*>(v), static_cast<T*>(o), lse, N, nqt, c2);
+                     static_cast<const T*>(v), static_cast<T*>(o), lse, N, nqt, c2, L);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -1086,18 +1151,147 @@ bool use_pingpong(int64_t bh, int64_t N) {
   return bh * ((N + 255) / 256) >= kNumCUs;
 }
 
-template <class E, class T>
+template <class E, class T, bool C>
 int launch16(int64_t bh, int64_t N, int64_t d, hipStream_t s, const void* q, const void* k,
-             const void* v, void* o, float* lse, float c2) {
+             const void* v, void* o, float* lse, float c2, const Layout& L) {
   if (use_pingpong(bh, N)) {
     const int64_t nqt = (N + 255) / 256;
-    if (bh * nqt > INT32_MAX) return ATTN_ERR_SHAPE;
-    auto kern = d == 128 ? attn_fwd_pp16<E, 128> : attn_fwd_pp16<E, 64>;
-    return launch<T>(kern, bh * nqt, kPPThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2);
+    auto kern = d == 128 ? attn_fwd_pp16<E, 128, C> : attn_fwd_pp16<E, 64, C>;
+    return launch<T>(kern, bh * nqt, kPPThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2, L);
   }
   const int64_t nqt = (N + 127) / 128;
-  auto kern = d == 128 ? attn_fwd_mfma16<E, 128> : attn_fwd_mfma16<E, 64>;
-  return launch<T>(kern, bh * nqt, kThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2);
+  auto kern = d == 128 ? attn_fwd_mfma16<E, 128, C> : attn_fwd_mfma16<E, 64, C>;
+  return launch<T>(kern, bh * nqt, kThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2, L);
+}
+
+template <bool C>
+int launch32(int64_t bh, int64_t N, int64_t d, hipStream_t s, const void* q, const void* k,
+             const void* v, void* o, float* lse, float c2, const Layout& L) {
+  const int64_t nqt = (N + 127) / 128;
+  auto kern = d == 128 ? attn_fwd_mfma32<128, C> : attn_fwd_mfma32<64, C>;
+  return launch<float>(kern, bh * nqt, kThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2, L);
+}
+
+// Byte ranges of a strided [B, H, N, d] tensor: the lowest and one past the
+// highest byte any element occupies (strides are non-negative).
+void span_of(const void* p, const int64_t (&st)[3], int64_t B, int64_t H, int64_t N, int64_t d,
+             size_t esize, uintptr_t* lo, uintptr_t* hi) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p);
+  const uint64_t last = (uint64_t)(B - 1) * st[0] + (uint64_t)(H - 1) * st[1] +
+                        (uint64_t)(N - 1) * st[2] + (uint64_t)(d - 1);
+  *lo = base;
+  *hi = base + (last + 1) * esize;
+}
+
+bool ranges_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+  return a0 < b1 && b0 < a1;
+}
+
+// Rows of one tensor never share bytes: either every (b, h, n) row has its
+// own d-element slot under the stride order, which holds when the strides,
+// sorted, each cover the extent of the dimensions below them.
+bool rows_disjoint(const int64_t (&st)[3], int64_t B, int64_t H, int64_t N, int64_t d) {
+  int64_t dims[3][2] = {{st[0], B}, {st[1], H}, {st[2], N}};
+  // sort by stride (three elements)
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (dims[j][0] < dims[i][0]) {
+        int64_t t0 = dims[i][0], t1 = dims[i][1];
+        dims[i][0] = dims[j][0], dims[i][1] = dims[j][1];
+        dims[j][0] = t0, dims[j][1] = t1;
+      }
+  int64_t extent = d;  // elements covered by one step of the next dimension
+  for (int i = 0; i < 3; ++i) {
+    if (dims[i][1] <= 1) continue;  // a dimension of size 1 never steps
+    if (dims[i][0] < extent) return false;
+    extent = dims[i][0] * dims[i][1];
+  }
+  return true;
+}
+
+int run_fwd(const attn_fwd_args_t& a) {
+  // --- validation: no HIP call before this block has passed -------------
+  const int64_t B = a.B, H = a.H, N = a.N, d = a.d;
+  if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
+  if (a.dtype != ATTN_DTYPE_F32 && a.dtype != ATTN_DTYPE_F16 && a.dtype != ATTN_DTYPE_BF16)
+    return ATTN_ERR_DTYPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!isfinite(a.scale)) return ATTN_ERR_SCALE;
+  if ((a.flags & ~ATTN_CAUSAL) != 0) return ATTN_ERR_FLAGS;
+  int64_t bh = 0, bhn = 0, elems = 0;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &elems))
+    return ATTN_ERR_SHAPE;
+  if (bhn == 0) return ATTN_OK;  // empty: nothing to launch
+  if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
+  if (a.q == nullptr || a.k == nullptr || a.v == nullptr || a.o == nullptr)
+    return ATTN_ERR_NULLPTR;
+  const size_t esize = a.dtype == ATTN_DTYPE_F32 ? 4 : 2;
+  if (elems > INT64_MAX / (int64_t)esize) return ATTN_ERR_SHAPE;
+  int64_t nblocks = 0;  // the largest grid: 128 query rows per block
+  if (!mul_ok(bh, (N + 127) / 128, &nblocks) || nblocks > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (H > INT32_MAX) return ATTN_ERR_SHAPE;
+
+  // strides: all zero means contiguous [B, H, N, d]
+  int64_t st[4][3];
+  const int64_t* given[4] = {a.q_stride, a.k_stride, a.v_stride, a.o_stride};
+  for (int t = 0; t < 4; ++t) {
+    const int64_t* g = given[t];
+    if (g[0] == 0 && g[1] == 0 && g[2] == 0) {
+      st[t][0] = H * N * d, st[t][1] = N * d, st[t][2] = d;
+    } else {
+      for (int i = 0; i < 3; ++i) {
+        if (g[i] < 0 || g[i] % 8 != 0 || g[i] > INT64_MAX / 4) return ATTN_ERR_LAYOUT;
+        st[t][i] = g[i];
+      }
+      if (st[t][2] < d) return ATTN_ERR_LAYOUT;  // rows of one head overlap
+      // the whole tensor must be addressable: sum of (dim - 1) * stride
+      int64_t x = 0, y = 0, z = 0;
+      if (!mul_ok(B - 1, st[t][0], &x) || !mul_ok(H - 1, st[t][1], &y) ||
+          !mul_ok(N - 1, st[t][2], &z) || x > INT64_MAX / 4 - y - z - d)
+        return ATTN_ERR_LAYOUT;
+    }
+    // the kernels address a head's rows with 32-bit byte offsets
+    if (N * st[t][2] * (int64_t)esize >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  }
+  if (!rows_disjoint(st[3], B, H, N, d)) return ATTN_ERR_LAYOUT;
+
+  auto misaligned = [](const void* p, uintptr_t al) {
+    return (reinterpret_cast<uintptr_t>(p) & (al - 1)) != 0;
+  };
+  if (misaligned(a.q, 16) || misaligned(a.k, 16) || misaligned(a.v, 16) ||
+      misaligned(a.o, 16) || (a.lse != nullptr && misaligned(a.lse, 4)))
+    return ATTN_ERR_ALIGN;
+  uintptr_t r[4][2];
+  const void* ptrs[4] = {a.q, a.k, a.v, a.o};
+  for (int t = 0; t < 4; ++t) span_of(ptrs[t], st[t], B, H, N, d, esize, &r[t][0], &r[t][1]);
+  for (int t = 0; t < 3; ++t)
+    if (ranges_overlap(r[3][0], r[3][1], r[t][0], r[t][1])) return ATTN_ERR_ALIAS;
+  if (a.lse != nullptr) {
+    const uintptr_t l0 = reinterpret_cast<uintptr_t>(a.lse), l1 = l0 + (size_t)bhn * 4;
+    for (int t = 0; t < 4; ++t)
+      if (ranges_overlap(l0, l1, r[t][0], r[t][1])) return ATTN_ERR_ALIAS;
+  }
+
+  // --- launch -------------------------------------------------------------
+  Layout L;
+  L.H = (int)H;
+  for (int i = 0; i < 3; ++i) {
+    L.q[i] = st[0][i], L.k[i] = st[1][i], L.v[i] = st[2][i], L.o[i] = st[3][i];
+  }
+  const float c2 = a.scale * kLog2e;
+  const bool causal = (a.flags & ATTN_CAUSAL) != 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
+  const void *q = a.q, *k = a.k, *v = a.v;
+  void* o = a.o;
+  float* lse = a.lse;
+  if (a.dtype == ATTN_DTYPE_BF16)
+    return causal ? launch16<Bf16T, uint16_t, true>(bh, N, d, s, q, k, v, o, lse, c2, L)
+                  : launch16<Bf16T, uint16_t, false>(bh, N, d, s, q, k, v, o, lse, c2, L);
+  if (a.dtype == ATTN_DTYPE_F16)
+    return causal ? launch16<F16T, uint16_t, true>(bh, N, d, s, q, k, v, o, lse, c2, L)
+                  : launch16<F16T, uint16_t, false>(bh, N, d, s, q, k, v, o, lse, c2, L);
+  return causal ? launch32<true>(bh, N, d, s, q, k, v, o, lse, c2, L)
+                : launch32<false>(bh, N, d, s, q, k, v, o, lse, c2, L);
 }
 
 }  // namespace
@@ -1105,44 +1299,19 @@ int launch16(int64_t bh, int64_t N, int64_t d, hipStream_t s, const void* q, con
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype,
                         void* stream) {
-  // --- validation: no HIP call before this block has passed -------------
-  if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
-  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16)
-    return ATTN_ERR_DTYPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
-  int64_t bh = 0, bhn = 0, elems = 0;
-  if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &elems))
-    return ATTN_ERR_SHAPE;
-  if (bhn == 0) return ATTN_OK;  // empty: nothing to launch
-  if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULLPTR;
-  const size_t esize = dtype == ATTN_DTYPE_F32 ? 4 : 2;
-  if (elems > INT64_MAX / (int64_t)esize) return ATTN_ERR_SHAPE;
-  int64_t nblocks = 0;  // the largest grid: 128 query rows per block
-  if (!mul_ok(bh, (N + 127) / 128, &nblocks) || nblocks > INT32_MAX) return ATTN_ERR_SHAPE;
-  auto misaligned = [](const void* p, uintptr_t a) {
-    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
-  };
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
-      (lse != nullptr && misaligned(lse, 4)))
-    return ATTN_ERR_ALIGN;
-  const size_t tbytes = (size_t)elems * esize, lbytes = (size_t)bhn * 4;
-  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
-      overlaps(o, tbytes, v, tbytes))
-    return ATTN_ERR_ALIAS;
-  if (lse != nullptr && (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) ||
-                         overlaps(lse, lbytes, v, tbytes) || overlaps(lse, lbytes, o, tbytes)))
-    return ATTN_ERR_ALIAS;
+  attn_fwd_args_t a;
+  memset(&a, 0, sizeof(a));
+  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
+  a.B = B, a.H = H, a.N = N, a.d = d;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.stream = stream;
+  return run_fwd(a);
+}
 
-  // --- launch -------------------------------------------------------------
-  const float c2 = scale * kLog2e;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == ATTN_DTYPE_BF16) return launch16<Bf16T, uint16_t>(bh, N, d, s, q, k, v, o, lse, c2);
-  if (dtype == ATTN_DTYPE_F16) return launch16<F16T, uint16_t>(bh, N, d, s, q, k, v, o, lse, c2);
-  const int64_t nqt = (N + 127) / 128;
-  auto kern = d == 128 ? attn_fwd_mfma32<128> : attn_fwd_mfma32<64>;
-  return launch<float>(kern, bh * nqt, kThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2);
+extern "C" int attn_fwd_ex(const attn_fwd_args_t* args) {
+  if (args == nullptr) return ATTN_ERR_NULLPTR;
+  return run_fwd(*args);
 }
 
 extern "C" const char* attn_strerror(int code) {
@@ -1156,8 +1325,10 @@ extern "C" const char* attn_strerror(int code) {
     case ATTN_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_ALIAS: return "an output overlaps an input (or lse overlaps o)";
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    case ATTN_ERR_FLAGS: return "unknown flag bits";
+    case ATTN_ERR_LAYOUT: return "invalid strides: negative, not a multiple of 8 elements, or overlapping output rows";
     default: return "unknown error code";
   }
 }
 
-extern "C" int attn_version(void) { return 100; }
+extern "C" int attn_version(void) { return 200; }

@@ -45,7 +45,10 @@ enum {
   ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite                           */
   ATTN_ERR_ALIGN = -6,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte  */
   ATTN_ERR_ALIAS = -7,    /* o or lse overlaps an input, or lse overlaps o      */
-  ATTN_ERR_HIP = -8       /* the kernel launch failed (hipGetLastError)         */
+  ATTN_ERR_HIP = -8,      /* the kernel launch failed (hipGetLastError)         */
+  ATTN_ERR_FLAGS = -9,    /* attn_fwd_ex: unknown bits in flags                 */
+  ATTN_ERR_LAYOUT = -10   /* attn_fwd_ex: a stride is negative, not a multiple
+                             of 8 elements, or rows of a head overlap           */
 };
 
 /* Largest sequence length accepted: per-head byte offsets and buffer sizes
@@ -81,6 +84,51 @@ enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype,
              void* stream);
+
+/* Flags of attn_fwd_ex. */
+#define ATTN_CAUSAL 1u /* query row i attends keys 0..i only */
+
+/*
+ * Arguments of attn_fwd_ex: those of attn_fwd, plus flags and tensor strides.
+ *
+ * flags   : 0, or ATTN_CAUSAL for the causal variant (page 1 section 4 notes
+ *           that practical kernels add a causal mask; page 3 section 3's
+ *           decoder layer masks future positions with -1e9 before the
+ *           softmax and section 6's wrapper passes a causal flag).  Query
+ *           row i then attends keys 0..i: s_ij for j > i is excluded
+ *           (probability exactly 0), and lse covers keys 0..i.
+ * *_stride: element strides of the batch, head and row dimensions of q, k,
+ *           v and o ({b, h, n}); the head dimension is always contiguous.
+ *           All three zero means contiguous [B, H, N, d] (strides
+ *           {H*N*d, N*d, d}); a [B, N, H, d] tensor has {N*H*d, d, H*d}.
+ *           Every stride must be a multiple of 8 (16-byte aligned rows) and
+ *           the (b, h, n) rows of o must not overlap.  lse is always
+ *           contiguous [B, H, N].
+ */
+typedef struct attn_fwd_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t B, H, N, d;
+  float scale;
+  int dtype;
+  unsigned flags;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  void* stream;
+} attn_fwd_args_t;
+
+/*
+ * attn_fwd_ex - attn_fwd with flags and strides (see attn_fwd_args_t).
+ * Same ownership, validation and return codes as attn_fwd, plus
+ * ATTN_ERR_FLAGS and ATTN_ERR_LAYOUT; args itself is read during the call
+ * only.  args == NULL returns ATTN_ERR_NULLPTR.
+ */
+int attn_fwd_ex(const attn_fwd_args_t* args);
 
 /* Static text for a return code (never NULL). */
 const char* attn_strerror(int code);

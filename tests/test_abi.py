@@ -97,3 +97,95 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.attn_fwd(q, q, q, torch.empty_like(q), None, 0.125)
+
+
+# ---------------------------------------------------------------------------
+# attn_fwd_ex: flags and strides
+# ---------------------------------------------------------------------------
+
+FLAGS, LAYOUT = -9, -10
+
+
+def ex_args(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=128, d=64, scale=0.125, dtype=BF16,
+            flags=0, qs=(0, 0, 0), ks=(0, 0, 0), vs=(0, 0, 0), os_=(0, 0, 0)):
+    from attention_attn_fwd_07_amd import _Args
+    a = _Args()
+    a.q, a.k, a.v, a.o, a.lse = q, k, v, o, lse
+    a.B, a.H, a.N, a.d, a.scale, a.dtype, a.flags = B, H, N, d, scale, dtype, flags
+    a.q_stride[:], a.k_stride[:], a.v_stride[:], a.o_stride[:] = qs, ks, vs, os_
+    a.stream = None
+    return a
+
+
+def call_ex(lib, **kw):
+    from attention_attn_fwd_07_amd import _Args
+    lib.attn_fwd_ex.argtypes = [ctypes.POINTER(_Args)]
+    lib.attn_fwd_ex.restype = ctypes.c_int
+    return lib.attn_fwd_ex(ctypes.byref(ex_args(**kw)))
+
+
+def test_args_struct_matches_the_header(tmp_path):
+    """The binding's ctypes mirror of attn_fwd_args_t has the C layout."""
+    import shutil
+    import subprocess
+    from attention_attn_fwd_07_amd import _Args
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in _Args._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "attn_fwd.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(attn_fwd_args_t));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(attn_fwd_args_t, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(_Args)
+    assert got[1:] == [getattr(_Args, f).offset for f in fields]
+
+
+def test_ex_null_args(lib):
+    lib.attn_fwd_ex.argtypes = [ctypes.c_void_p]
+    lib.attn_fwd_ex.restype = ctypes.c_int
+    assert lib.attn_fwd_ex(None) == NULLPTR
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=2), FLAGS), (dict(flags=0x80000001), FLAGS),
+    (dict(qs=(0, 0, -64)), LAYOUT), (dict(ks=(2 * 128 * 64, 128 * 64, 60)), LAYOUT),
+    (dict(vs=(-8, 8, 64)), LAYOUT), (dict(os_=(2 * 128 * 64, 128 * 64, 32)), LAYOUT),
+    # o rows of different heads collide: head stride 32 < d = 64
+    (dict(os_=(2 * 128 * 128, 32, 128)), LAYOUT),
+    # o rows of the two batches collide: batch stride 32 < d = 64
+    (dict(B=2, os_=(32, 128 * 256, 256)), LAYOUT),
+    (dict(B=0, flags=2), FLAGS),
+    (dict(N=0, qs=(0, 0, 3)), OK),   # empty input returns before strides are looked at
+    (dict(q=None, flags=1), NULLPTR),
+])
+def test_ex_rejects_before_any_hip_call(lib, kw, code):
+    assert call_ex(lib, **kw) == code
+
+
+def test_rows_disjoint_interleaved_heads_are_valid():
+    # [B, N, H, d] viewed as [B, H, N, d]: head stride d, row stride H d.  A
+    # valid layout, accepted by the host checks (it would launch, so only the
+    # disjointness logic is exercised here, through the Python stride helper).
+    import torch
+    from attention_attn_fwd_07_amd import _strides
+    t = torch.zeros(1, 128, 2, 64).transpose(1, 2)
+    assert _strides(t) == (128 * 2 * 64, 64, 128)
+
+
+def test_ex_strided_alias_uses_the_strided_extent(lib):
+    # o written with BNHD strides spans 2*128*64 elements; an lse placed inside
+    # that span is an alias even though it lies beyond o's first head.
+    bnhd = (128 * 2 * 64, 64, 2 * 64)
+    assert call_ex(lib, os_=bnhd, lse=O + 2 * 64 * 2 * 100) == ALIAS
+
+
+def test_ex_head_bytes_limit(lib):
+    # a head's rows must be addressable with 32-bit byte offsets in the kernels
+    assert call_ex(lib, N=1 << 20, ks=(0, 0, 2048), d=64) == SHAPE

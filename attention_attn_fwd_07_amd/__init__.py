@@ -9,6 +9,7 @@ GPU is present, calls raise.
     o, lse = fwd(q, k, v)                  # allocate outputs, scale = 1/sqrt(d)
     attn_fwd(q, k, v, o, lse, scale)       # caller-owned outputs, async launch
     p = plan(q, k, v, o, lse, scale); p()  # checked once, then relaunched cheaply
+    o, lse = fwd_splitkv(q, k, v, splits=8)  # keys split over 8 blocks, then merged
 
 Tensors are ``[B, H, N, d]`` fp32/fp16/bf16 with d in {64, 128}; the head
 dimension must be contiguous, the other three dimensions may have any strides
@@ -28,7 +29,7 @@ import os
 from .build import LIB
 
 __all__ = ["attn_fwd", "fwd", "plan", "Plan", "attn_strerror", "attn_version", "library_path",
-           "AttnError", "ATTN_CAUSAL"]
+           "AttnError", "ATTN_CAUSAL", "splitkv_workspace_size", "fwd_splitkv"]
 
 ATTN_OK = 0
 ATTN_ERR_HIP = -8
@@ -78,6 +79,10 @@ def _load():
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd_ex.argtypes = [ctypes.POINTER(_Args)]
     lib.attn_fwd_ex.restype = ctypes.c_int
+    lib.attn_fwd_splitkv.argtypes = [ctypes.POINTER(_Args), ctypes.c_int, vp, ctypes.c_size_t]
+    lib.attn_fwd_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_splitkv_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.attn_fwd_splitkv_workspace.restype = ctypes.c_size_t
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -158,7 +163,8 @@ class Plan:
     keeps the tensors alive and unchanged in shape while the plan is used.
     """
 
-    def __init__(self, q, k, v, o, lse, scale: float, stream=None, causal: bool = False):
+    def __init__(self, q, k, v, o, lse, scale: float, stream=None, causal: bool = False,
+                 splits: int = 0, workspace=None):
         torch = _torch()
         code_dtype = _check(q, k, v, o, lse)
         B, H, N, d = (int(x) for x in q.shape)
@@ -167,7 +173,7 @@ class Plan:
         elif hasattr(stream, "cuda_stream"):
             stream = stream.cuda_stream
         self.device = q.device
-        self._fn = _load().attn_fwd_ex
+        lib = _load()
         a = _Args()
         a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
         a.lse = lse.data_ptr() if lse is not None else None
@@ -182,19 +188,61 @@ class Plan:
         a.stream = stream
         self._args = a
         self._ref = ctypes.byref(a)
-        self._tensors = (q, k, v, o, lse)  # keep the storage alive
+        if splits:
+            if workspace is None:
+                raise ValueError("the split-KV path needs a workspace tensor")
+            if workspace.device != q.device or not workspace.is_contiguous():
+                raise ValueError("workspace must be contiguous and on q's device")
+            nbytes = workspace.numel() * workspace.element_size()
+            fn, ws = lib.attn_fwd_splitkv, ctypes.c_void_p(workspace.data_ptr())
+            self._call = lambda: fn(self._ref, int(splits), ws, nbytes)
+        else:
+            fn = lib.attn_fwd_ex
+            self._call = lambda: fn(self._ref)
+        self._tensors = (q, k, v, o, lse, workspace)  # keep the storage alive
 
     def __call__(self) -> None:
-        rc = self._fn(self._ref)
+        rc = self._call()
         if rc != ATTN_OK:
             _raise_for(rc)
 
 
-def plan(q, k, v, o, lse, scale: float, stream=None, causal: bool = False) -> Plan:
-    """Check the arguments of ``attn_fwd_ex`` once and return a relaunchable call.
+def plan(q, k, v, o, lse, scale: float, stream=None, causal: bool = False, splits: int = 0,
+         workspace=None) -> Plan:
+    """Check the arguments of ``attn_fwd_ex`` (or, with ``splits``, of
+    ``attn_fwd_splitkv``) once and return a relaunchable call.
 
     q's device must be the current device whenever the plan is called."""
-    return Plan(q, k, v, o, lse, scale, stream, causal)
+    return Plan(q, k, v, o, lse, scale, stream, causal, splits, workspace)
+
+
+def splitkv_workspace_size(B: int, H: int, N: int, d: int, splits: int) -> int:
+    """Bytes of workspace ``attn_fwd_splitkv`` needs (0 for empty sizes)."""
+    return int(_load().attn_fwd_splitkv_workspace(B, H, N, d, splits))
+
+
+def fwd_splitkv(q, k, v, scale: float | None = None, splits: int = 4, workspace=None,
+                return_lse: bool = True):
+    """``fwd`` through the split-KV path: each head's keys split into up to
+    ``splits`` ranges handled by separate blocks, the partial results merged
+    by a second kernel.  Allocates the workspace if none is given."""
+    torch = _torch()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    B, H, N, d = (int(x) for x in q.shape)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = (torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+           if return_lse else None)
+    if workspace is None:
+        nbytes = splitkv_workspace_size(B, H, N, d, splits)
+        workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=q.device)
+    p = Plan(q, k, v, o, lse, scale, None, False, splits, workspace)
+    if torch.cuda.current_device() == p.device.index:
+        p()
+    else:
+        with torch.cuda.device(p.device):
+            p()
+    return o, lse
 
 
 def attn_fwd(q, k, v, o, lse, scale: float, stream=None, causal: bool = False) -> None:

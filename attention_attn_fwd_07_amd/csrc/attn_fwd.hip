@@ -77,6 +77,54 @@ struct Layout {
   }
 };
 
+// Key split of the split-KV path.  With len > 0, block (x, y) of the grid
+// covers key rows y*len .. min(N, (y+1)*len) - 1 only and writes its own
+// normalised output and log-sum-exp, in fp32, to opart[y][b*H+h][row][d] and
+// lpart[y][b*H+h][row]; a second kernel merges the splits.  len == 0: one
+// block covers all keys and writes the final O and lse.
+struct Split {
+  int len;
+  float* opart;
+  float* lpart;
+  __device__ __forceinline__ int first_key() const { return len ? (int)blockIdx.y * len : 0; }
+  __device__ __forceinline__ int keys(int N) const { return len ? min(N - first_key(), len) : N; }
+};
+
+// Stores of one query row's result (the lane's 16 columns of each 32-column
+// block, rows of O^T's C fragment): the final O rounded to the element type,
+// or in split mode the fp32 partial O and lse.
+template <class E, int D>
+__device__ __forceinline__ void store_row16(uint16_t* __restrict__ Oh, float* __restrict__ LSE,
+                                           const Split& sp, const Layout& L, int bh, int nbh,
+                                           int N, int qrow, const f32x16 (&acc)[D / 32],
+                                           float inv, float lse) {
+  const int hh = (threadIdx.x & 63) >> 5;
+  if (sp.len) {
+    const size_t r = ((size_t)blockIdx.y * nbh + bh) * N + qrow;
+    float* op = sp.opart + r * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * g + 4 * hh) =
+            (f32x4){acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv,
+                    acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+    if (hh == 0) sp.lpart[r] = lse;
+    return;
+  }
+  uint16_t* op = Oh + (size_t)qrow * L.o[2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = 32 * db + 8 * g + 4 * hh;
+      const u32x2 w = (u32x2){E::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                              E::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+      *reinterpret_cast<u32x2*>(op + col) = w;
+    }
+  if (LSE != nullptr && hh == 0) LSE[(size_t)bh * N + qrow] = lse;
+}
+
 // ---------------------------------------------------------------------------
 // element traits for the 16-bit paths
 // ---------------------------------------------------------------------------
@@ -281,16 +329,17 @@ struct TileLoader {
     voff = (uint32_t)(r0 * vrs + ((p ^ swz_v<D>(r0)) << 4));
   }
 
-  // Rows j0 .. j0+63 of one tensor (K or V, with its lane offset and row
-  // stride rs in bytes) -> xb, stored densely (ROWB bytes per row) in LDS.
+  // Rows j0 .. j0+63 (j0 < N) of one tensor (K or V, with its lane offset and
+  // row stride rs in bytes) -> xb, stored densely (ROWB bytes per row) in LDS.
+  // One descriptor per tile, from row j0 to row N; load u adds its rows to
+  // the per-lane offset, which is what the hardware range check applies to.
   __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int rs, int j0,
                                        int N, lds_u8* xb) const {
+    const i32x4 rsrc = buffer_rsrc(Xb + (size_t)j0 * rs, (N - j0) * rs);  // N*rs < 2^31
 #pragma unroll
     for (int u = 0; u < G::LOADS_PER_WAVE; ++u) {
-      const int row = j0 + u * STEP_ROWS;
-      const int bytes = N > row ? (N - row) * rs : 0;  // N * rs < 2^31 (checked on the host)
       const int blk = u * NW + wave;
-      lds_dma16(buffer_rsrc(Xb + (size_t)row * rs, bytes), off, lds_addr(xb + blk * G::LOADB));
+      lds_dma16(rsrc, off + (uint32_t)(u * STEP_ROWS * rs), lds_addr(xb + blk * G::LOADB));
     }
   }
   __device__ __forceinline__ void load_k(const unsigned char* Kb, int j0, int N,
@@ -471,7 +520,7 @@ template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                     float* __restrict__ LSE, int N, int nqt, float c2, Layout L) {
+                     float* __restrict__ LSE, int N, int nqt, float c2, Layout L, Split sp) {
   using G = Geo16<D, 4>;
   constexpr int BM = 128;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
@@ -488,20 +537,24 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
   const uint16_t* const Qh = Q + L.base(L.q, bh);
   uint16_t* const Oh = O + L.base(L.o, bh);
-  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + L.base(L.k, bh));
-  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + L.base(L.v, bh));
+  // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
+  const int kb0 = sp.first_key(), Nk = sp.keys(N);
+  const unsigned char* Kb =
+      reinterpret_cast<const unsigned char*>(K + L.base(L.k, bh) + (long long)kb0 * L.k[2]);
+  const unsigned char* Vb =
+      reinterpret_cast<const unsigned char*>(V + L.base(L.v, bh) + (long long)kb0 * L.v[2]);
 
-  const int ntiles = key_tiles<CAUSAL>(N, qt * BM, BM, G::BN);
+  const int ntiles = key_tiles<CAUSAL>(Nk, qt * BM, BM, G::BN);
   const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
                                (int)(L.k[2] * 2), (int)(L.v[2] * 2));
-  loader.load_k(Kb, 0, N, kbuf0);
-  loader.load_v(Vb, 0, N, vbuf0);
-  if (ntiles > 1) loader.load_k(Kb, G::BN, N, kbuf1);
+  loader.load_k(Kb, 0, Nk, kbuf0);
+  loader.load_v(Vb, 0, Nk, vbuf0);
+  if (ntiles > 1) loader.load_k(Kb, G::BN, Nk, kbuf1);
 
   // Q fragment, resident for the whole key loop: lane (li, hh) holds
   // d = 16 ks + 8 hh + [0, 8) of query row qrow.
   const int qrow = qt * BM + wave * 32 + li;
-  const KeyLimit<CAUSAL> kl(N, qrow, qt * BM + wave * 32);
+  const KeyLimit<CAUSAL> kl(Nk, qrow, qt * BM + wave * 32);
   u32x4 qf[G::KS];
   if (qrow < N) {
     const u32x4* qp = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * L.q[2] + 8 * hh);
@@ -528,8 +581,8 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   auto body = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], const lds_u8* kb_next,
                   const lds_u8* vb_cur, lds_u8* kb_load, lds_u8* vb_load) {
     const int j1 = (t + 1) * G::BN;
-    if (t + 2 < ntiles) loader.load_k(Kb, j1 + G::BN, N, kb_load);
-    loader.load_v(Vb, j1, N, vb_load);
+    if (t + 2 < ntiles) loader.load_k(Kb, j1 + G::BN, Nk, kb_load);
+    loader.load_v(Vb, j1, Nk, vb_load);
     u32x4 pb[2][2];
     if (CAUSAL && kl.partial(t * G::BN, G::BN))  // a diagonal tile (others are full)
       l += softmax16<E, true>(cur, m, c2, pb, t * G::BN, kl.lane_lim);
@@ -568,19 +621,9 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
-  if (qrow < N) {
-    uint16_t* op = Oh + (size_t)qrow * L.o[2];
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * hh;
-        const u32x2 w = (u32x2){E::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
-                                E::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + col) = w;
-      }
-    if (LSE != nullptr && hh == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
-  }
+  if (qrow < N)
+    store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv,
+                      (m + log2f(lt)) * kLn2);
 }
 
 // --- MFMA phase with lean registers ---------------------------------------
@@ -765,7 +808,7 @@ template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                   float* __restrict__ LSE, int N, int nqt, float c2, Layout L) {
+                   float* __restrict__ LSE, int N, int nqt, float c2, Layout L, Split sp) {
   using G = Geo16<D, 8>;
   constexpr int BM = 256;
   constexpr uint32_t TB = G::TILEB;
@@ -783,10 +826,14 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
   const uint16_t* const Qh = Q + L.base(L.q, bh);
   uint16_t* const Oh = O + L.base(L.o, bh);
-  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + L.base(L.k, bh));
-  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + L.base(L.v, bh));
+  // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
+  const int kb0 = sp.first_key(), Nk = sp.keys(N);
+  const unsigned char* Kb =
+      reinterpret_cast<const unsigned char*>(K + L.base(L.k, bh) + (long long)kb0 * L.k[2]);
+  const unsigned char* Vb =
+      reinterpret_cast<const unsigned char*>(V + L.base(L.v, bh) + (long long)kb0 * L.v[2]);
 
-  const int T = key_tiles<CAUSAL>(N, qt * BM, BM, G::BN);
+  const int T = key_tiles<CAUSAL>(Nk, qt * BM, BM, G::BN);
   // Group 0 loads V tiles, group 1 K tiles; all values here are wave-uniform.
   const PPLoader<D> loader(wave & 3, (int)(L.k[2] * 2), (int)(L.v[2] * 2));
   constexpr int LPW = PPLoader<D>::LPW;
@@ -795,7 +842,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int xrs = grp == 0 ? loader.vrs : loader.krs;
   const uint32_t xring = lbase + (grp == 0 ? VRING : 0u);
   auto load_tile = [&](int j) __attribute__((always_inline)) {  // tile j of this group's tensor, into ring slot j % 4
-    loader.load(Xb, xoff, xrs, j * G::BN, N, xring + (uint32_t)(j % kRing) * TB);
+    loader.load(Xb, xoff, xrs, j * G::BN, Nk, xring + (uint32_t)(j % kRing) * TB);
   };
   // Wait until at most the loads of tiles j+1 and j+2 (those that exist) are
   // still in flight, i.e. until tile j has landed (loads complete in order).
@@ -817,7 +864,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 
   const int qrow = qt * BM + wave * 32 + li;
-  const KeyLimit<CAUSAL> kl(N, qrow, qt * BM + wave * 32);
+  const KeyLimit<CAUSAL> kl(Nk, qrow, qt * BM + wave * 32);
   u32x4 qf[G::KS];
   if (qrow < N) {
     const u32x4* qp = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * L.q[2] + 8 * hh);
@@ -921,19 +968,9 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
-  if (qrow < N) {
-    uint16_t* op = Oh + (size_t)qrow * L.o[2];
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * hh;
-        const u32x2 w = (u32x2){E::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
-                                E::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + col) = w;
-      }
-    if (LSE != nullptr && hh == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
-  }
+  if (qrow < N)
+    store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv,
+                      (m + log2f(lt)) * kLn2);
 }
 
 // ---------------------------------------------------------------------------
@@ -964,7 +1001,7 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c2, Layout L) {
+    float* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c2, Layout L, Split sp) {
   using G = Geo32<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM];
 
@@ -974,14 +1011,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
   const float* Qh = Q + L.base(L.q, bh);
-  const float* Kh = K + L.base(L.k, bh);
-  const float* Vh = V + L.base(L.v, bh);
+  // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
+  const int kb0 = sp.first_key(), Nk = sp.keys(N);
+  const float* Kh = K + L.base(L.k, bh) + (long long)kb0 * L.k[2];
+  const float* Vh = V + L.base(L.v, bh) + (long long)kb0 * L.v[2];
   float* const Oh = O + L.base(L.o, bh);
 
   // Contraction index of K*Q^T: lane half hh covers d in [hh*D/2, (hh+1)*D/2),
   // one d per MFMA k-step.
   const int qrow = qt * G::BM + wave * 32 + li;
-  const KeyLimit<CAUSAL> kl(N, qrow, qt * G::BM + wave * 32);
+  const KeyLimit<CAUSAL> kl(Nk, qrow, qt * G::BM + wave * 32);
   float qf[G::QV];
   if (qrow < N) {
     const f32x4* qp = reinterpret_cast<const f32x4*>(Qh + (size_t)qrow * L.q[2] + hh * G::QV);
@@ -1000,14 +1039,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
   float m = -INFINITY, l = 0.f;
 
-  const int ntiles = key_tiles<CAUSAL>(N, qt * G::BM, G::BM, G::BN);
+  const int ntiles = key_tiles<CAUSAL>(Nk, qt * G::BM, G::BM, G::BN);
   f32x4 kr[G::CPT], vr[G::CPT];
   auto gload = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < G::CPT; ++u) {
       const int ci = threadIdx.x + u * kThreads;
       const int row = ci / G::CH, c = ci % G::CH;
-      if (j0 + row < N) {
+      if (j0 + row < Nk) {
         kr[u] = *reinterpret_cast<const f32x4*>(Kh + (size_t)(j0 + row) * L.k[2] + c * 4);
         vr[u] = *reinterpret_cast<const f32x4*>(Vh + (size_t)(j0 + row) * L.v[2] + c * 4);
       } else {
@@ -1099,7 +1138,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
   if (qrow < N) {
-    float* op = Oh + (size_t)qrow * L.o[2];
+    float* op;
+    if (sp.len) {
+      const size_t r = ((size_t)blockIdx.y * (gridDim.x / nqt) + bh) * N + qrow;
+      op = sp.opart + r * D;
+      if (hh == 0) sp.lpart[r] = (m + log2f(lt)) * kLn2;
+    } else {
+      op = Oh + (size_t)qrow * L.o[2];
+      if (LSE != nullptr && hh == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+    }
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -1109,8 +1156,65 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
             (f32x4){acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv,
                     acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
       }
-    if (LSE != nullptr && hh == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
   }
+}
+
+// ---------------------------------------------------------------------------
+// split-KV merge
+// ---------------------------------------------------------------------------
+//
+// Each split of a row's keys produced its own normalised output O_s and
+// log-sum-exp lse_s.  They combine exactly as the per-block statistics of a
+// long softmax row do (page 3 section 1.1: the maxima and sums of the blocks
+// merge into the row's; section 5 stores lse for this purpose):
+//   lse = ln sum_s exp(lse_s),   O = sum_s exp(lse_s - lse) O_s.
+// One thread handles four consecutive columns of one row; the sum runs with
+// the largest lse_s subtracted, as a softmax over the splits.
+struct OutF32 {
+  static __device__ __forceinline__ void store4(float* p, f32x4 v) {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+};
+template <class E>
+struct Out16 {
+  static __device__ __forceinline__ void store4(uint16_t* p, f32x4 v) {
+    *reinterpret_cast<u32x2*>(p) = (u32x2){E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+  }
+};
+
+constexpr int kMergeThreads = 256;
+
+template <class OUT, class T, int D>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* __restrict__ opart,
+                                                            const float* __restrict__ lpart,
+                                                            T* __restrict__ O,
+                                                            float* __restrict__ LSE, int N,
+                                                            int nbh, int S, Layout L) {
+  constexpr int TPR = D / 4;                // threads per row
+  constexpr int RPB = kMergeThreads / TPR;  // rows per block
+  const int r = blockIdx.x * RPB + (int)threadIdx.x / TPR;  // row of the B*H*N rows
+  const int c = 4 * ((int)threadIdx.x % TPR);
+  if (r >= nbh * N) return;
+  const size_t plane = (size_t)nbh * N;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, lpart[sp * plane + r]);
+  float sum = 0.f;
+  f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < S; ++sp) {
+    const size_t rs = sp * plane + r;
+    const float w = fast_exp2((lpart[rs] - mx) * kLog2e);
+    sum += w;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(opart + rs * D + c);
+    o[0] = fmaf(w, x[0], o[0]);
+    o[1] = fmaf(w, x[1], o[1]);
+    o[2] = fmaf(w, x[2], o[2]);
+    o[3] = fmaf(w, x[3], o[3]);
+  }
+  const float inv = 1.0f / sum;
+  o[0] *= inv, o[1] *= inv, o[2] *= inv, o[3] *= inv;
+  const int bh = r / N, i = r - bh * N;
+  OUT::store4(O + L.base(L.o, bh) + (long long)i * L.o[2] + c, o);
+  if (LSE != nullptr && c == 0) LSE[r] = mx + log2f(sum) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1127,13 +1231,27 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// Everything a launch needs besides the kernel choice.
+struct Launch {
+  hipStream_t stream;
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  int64_t bh, N, d;
+  float c2;
+  Layout L;
+  Split sp;    // sp.len == 0: no split
+  int splits;  // grid y (1 without a split)
+};
+
 template <class T>
-int launch(void (*kernel)(const T*, const T*, const T*, T*, float*, int, int, float, Layout),
-           int64_t nblocks, int threads, hipStream_t stream, const void* q, const void* k,
-           const void* v, void* o, float* lse, int N, int nqt, float c2, const Layout& L) {
-  hipLaunchKernelGGL(kernel, dim3((unsigned)nblocks), dim3(threads), 0, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(k),
-                     static_cast<const T*>(v), static_cast<T*>(o), lse, N, nqt, c2, L);
+int launch(void (*kernel)(const T*, const T*, const T*, T*, float*, int, int, float, Layout,
+                          Split),
+           int64_t nblocks, int threads, int nqt, const Launch& a) {
+  hipLaunchKernelGGL(kernel, dim3((unsigned)nblocks, (unsigned)a.splits), dim3(threads), 0,
+                     a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, (int)a.N, nqt,
+                     a.c2, a.L, a.sp);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -1144,32 +1262,41 @@ constexpr int kNumCUs = 256;  // MI355X
 // pipelined kernel (128 rows per block, up to two blocks per CU).  The
 // environment variable ATTN_FWD_KERNEL=pingpong|pipelined forces one (for
 // tests and sweeps).
-bool use_pingpong(int64_t bh, int64_t N) {
+bool use_pingpong(int64_t blocks256) {
   const char* env = getenv("ATTN_FWD_KERNEL");
   if (env != nullptr && strcmp(env, "pingpong") == 0) return true;
   if (env != nullptr && strcmp(env, "pipelined") == 0) return false;
-  return bh * ((N + 255) / 256) >= kNumCUs;
+  return blocks256 >= kNumCUs;
 }
 
 template <class E, class T, bool C>
-int launch16(int64_t bh, int64_t N, int64_t d, hipStream_t s, const void* q, const void* k,
-             const void* v, void* o, float* lse, float c2, const Layout& L) {
-  if (use_pingpong(bh, N)) {
-    const int64_t nqt = (N + 255) / 256;
-    auto kern = d == 128 ? attn_fwd_pp16<E, 128, C> : attn_fwd_pp16<E, 64, C>;
-    return launch<T>(kern, bh * nqt, kPPThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2, L);
+int launch16(const Launch& a) {
+  if (use_pingpong(a.bh * ((a.N + 255) / 256) * a.splits)) {
+    const int64_t nqt = (a.N + 255) / 256;
+    auto kern = a.d == 128 ? attn_fwd_pp16<E, 128, C> : attn_fwd_pp16<E, 64, C>;
+    return launch<T>(kern, a.bh * nqt, kPPThreads, (int)nqt, a);
   }
-  const int64_t nqt = (N + 127) / 128;
-  auto kern = d == 128 ? attn_fwd_mfma16<E, 128, C> : attn_fwd_mfma16<E, 64, C>;
-  return launch<T>(kern, bh * nqt, kThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2, L);
+  const int64_t nqt = (a.N + 127) / 128;
+  auto kern = a.d == 128 ? attn_fwd_mfma16<E, 128, C> : attn_fwd_mfma16<E, 64, C>;
+  return launch<T>(kern, a.bh * nqt, kThreads, (int)nqt, a);
 }
 
 template <bool C>
-int launch32(int64_t bh, int64_t N, int64_t d, hipStream_t s, const void* q, const void* k,
-             const void* v, void* o, float* lse, float c2, const Layout& L) {
-  const int64_t nqt = (N + 127) / 128;
-  auto kern = d == 128 ? attn_fwd_mfma32<128, C> : attn_fwd_mfma32<64, C>;
-  return launch<float>(kern, bh * nqt, kThreads, s, q, k, v, o, lse, (int)N, (int)nqt, c2, L);
+int launch32(const Launch& a) {
+  const int64_t nqt = (a.N + 127) / 128;
+  auto kern = a.d == 128 ? attn_fwd_mfma32<128, C> : attn_fwd_mfma32<64, C>;
+  return launch<float>(kern, a.bh * nqt, kThreads, (int)nqt, a);
+}
+
+template <class OUT, class T>
+int launch_merge(const Launch& a) {
+  const int64_t rows = a.bh * a.N;
+  const int tpr = (int)a.d / 4, rpb = kMergeThreads / tpr;
+  auto kern = a.d == 128 ? attn_merge<OUT, T, 128> : attn_merge<OUT, T, 64>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kMergeThreads), 0,
+                     a.stream, a.sp.opart, a.sp.lpart, static_cast<T*>(a.o), a.lse, (int)a.N,
+                     (int)a.bh, a.splits, a.L);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 // Byte ranges of a strided [B, H, N, d] tensor: the lowest and one past the
@@ -1209,7 +1336,17 @@ bool rows_disjoint(const int64_t (&st)[3], int64_t B, int64_t H, int64_t N, int6
   return true;
 }
 
-int run_fwd(const attn_fwd_args_t& a) {
+// Keys per split (a multiple of the 64-key tile) and the number of non-empty
+// splits for a requested split count.
+void split_plan(int64_t N, int requested, int64_t* len, int* splits) {
+  const int64_t tiles = (N + 63) / 64;
+  const int64_t per = (tiles + requested - 1) / requested;
+  *len = per * 64;
+  *splits = (int)((tiles + per - 1) / per);
+}
+
+// The plain path (splits == 0), or the split-KV path with its workspace.
+int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t ws_bytes = 0) {
   // --- validation: no HIP call before this block has passed -------------
   const int64_t B = a.B, H = a.H, N = a.N, d = a.d;
   if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
@@ -1218,6 +1355,8 @@ int run_fwd(const attn_fwd_args_t& a) {
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(a.scale)) return ATTN_ERR_SCALE;
   if ((a.flags & ~ATTN_CAUSAL) != 0) return ATTN_ERR_FLAGS;
+  if (splits != 0 && (splits < 1 || splits > ATTN_MAX_SPLITS)) return ATTN_ERR_SPLITS;
+  if (splits != 0 && (a.flags & ATTN_CAUSAL) != 0) return ATTN_ERR_FLAGS;
   int64_t bh = 0, bhn = 0, elems = 0;
   if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &elems))
     return ATTN_ERR_SHAPE;
@@ -1271,27 +1410,50 @@ int run_fwd(const attn_fwd_args_t& a) {
     for (int t = 0; t < 4; ++t)
       if (ranges_overlap(l0, l1, r[t][0], r[t][1])) return ATTN_ERR_ALIAS;
   }
+  int64_t split_len = 0;
+  int nsplit = 1;
+  if (splits != 0) {
+    split_plan(N, splits, &split_len, &nsplit);
+    if (ws == nullptr) return ATTN_ERR_NULLPTR;
+    if (misaligned(ws, 16)) return ATTN_ERR_ALIGN;
+    int64_t need = 0;
+    if (!mul_ok(bhn, (d + 1) * 4, &need) || !mul_ok(need, nsplit, &need)) return ATTN_ERR_SHAPE;
+    if (ws_bytes < (uint64_t)need) return ATTN_ERR_WORKSPACE;
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(ws), w1 = w0 + (size_t)need;
+    for (int t = 0; t < 4; ++t)
+      if (ranges_overlap(w0, w1, r[t][0], r[t][1])) return ATTN_ERR_ALIAS;
+    if (a.lse != nullptr) {
+      const uintptr_t l0 = reinterpret_cast<uintptr_t>(a.lse), l1 = l0 + (size_t)bhn * 4;
+      if (ranges_overlap(w0, w1, l0, l1)) return ATTN_ERR_ALIAS;
+    }
+  }
 
   // --- launch -------------------------------------------------------------
-  Layout L;
-  L.H = (int)H;
+  Launch x;
+  x.stream = reinterpret_cast<hipStream_t>(a.stream);
+  x.q = a.q, x.k = a.k, x.v = a.v, x.o = a.o, x.lse = a.lse;
+  x.bh = bh, x.N = N, x.d = d;
+  x.c2 = a.scale * kLog2e;
+  x.L.H = (int)H;
   for (int i = 0; i < 3; ++i) {
-    L.q[i] = st[0][i], L.k[i] = st[1][i], L.v[i] = st[2][i], L.o[i] = st[3][i];
+    x.L.q[i] = st[0][i], x.L.k[i] = st[1][i], x.L.v[i] = st[2][i], x.L.o[i] = st[3][i];
   }
-  const float c2 = a.scale * kLog2e;
+  x.splits = nsplit;
+  x.sp.len = (int)split_len;
+  x.sp.opart = splits ? static_cast<float*>(ws) : nullptr;
+  x.sp.lpart = splits ? static_cast<float*>(ws) + (size_t)nsplit * bhn * d : nullptr;
   const bool causal = (a.flags & ATTN_CAUSAL) != 0;
-  hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
-  const void *q = a.q, *k = a.k, *v = a.v;
-  void* o = a.o;
-  float* lse = a.lse;
+  int rc;
   if (a.dtype == ATTN_DTYPE_BF16)
-    return causal ? launch16<Bf16T, uint16_t, true>(bh, N, d, s, q, k, v, o, lse, c2, L)
-                  : launch16<Bf16T, uint16_t, false>(bh, N, d, s, q, k, v, o, lse, c2, L);
-  if (a.dtype == ATTN_DTYPE_F16)
-    return causal ? launch16<F16T, uint16_t, true>(bh, N, d, s, q, k, v, o, lse, c2, L)
-                  : launch16<F16T, uint16_t, false>(bh, N, d, s, q, k, v, o, lse, c2, L);
-  return causal ? launch32<true>(bh, N, d, s, q, k, v, o, lse, c2, L)
-                : launch32<false>(bh, N, d, s, q, k, v, o, lse, c2, L);
+    rc = causal ? launch16<Bf16T, uint16_t, true>(x) : launch16<Bf16T, uint16_t, false>(x);
+  else if (a.dtype == ATTN_DTYPE_F16)
+    rc = causal ? launch16<F16T, uint16_t, true>(x) : launch16<F16T, uint16_t, false>(x);
+  else
+    rc = causal ? launch32<true>(x) : launch32<false>(x);
+  if (rc != ATTN_OK || !splits) return rc;
+  if (a.dtype == ATTN_DTYPE_BF16) return launch_merge<Out16<Bf16T>, uint16_t>(x);
+  if (a.dtype == ATTN_DTYPE_F16) return launch_merge<Out16<F16T>, uint16_t>(x);
+  return launch_merge<OutF32, float>(x);
 }
 
 }  // namespace
@@ -1314,6 +1476,29 @@ extern "C" int attn_fwd_ex(const attn_fwd_args_t* args) {
   return run_fwd(*args);
 }
 
+extern "C" size_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
+                                             int splits) {
+  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128) || splits < 1 ||
+      splits > ATTN_MAX_SPLITS)
+    return 0;
+  int64_t bh = 0, bhn = 0, per = 0;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, (d + 1) * 4, &per)) return 0;
+  if (bhn == 0) return 0;
+  int64_t len = 0;
+  int nsplit = 1;
+  split_plan(N, splits, &len, &nsplit);
+  int64_t total = 0;
+  if (!mul_ok(per, nsplit, &total)) return 0;
+  return (size_t)total;
+}
+
+extern "C" int attn_fwd_splitkv(const attn_fwd_args_t* args, int splits, void* workspace,
+                                size_t workspace_bytes) {
+  if (args == nullptr) return ATTN_ERR_NULLPTR;
+  if (splits < 1 || splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
+  return run_fwd(*args, splits, workspace, workspace_bytes);
+}
+
 extern "C" const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";
@@ -1325,7 +1510,9 @@ extern "C" const char* attn_strerror(int code) {
     case ATTN_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_ALIAS: return "an output overlaps an input (or lse overlaps o)";
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
-    case ATTN_ERR_FLAGS: return "unknown flag bits";
+    case ATTN_ERR_FLAGS: return "unknown flag bits, or a flag the split-KV path does not take";
+    case ATTN_ERR_SPLITS: return "split count out of range (1 .. ATTN_MAX_SPLITS)";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_fwd_splitkv_workspace()";
     case ATTN_ERR_LAYOUT: return "invalid strides: negative, not a multiple of 8 elements, or overlapping output rows";
     default: return "unknown error code";
   }

@@ -20,6 +20,7 @@
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -47,9 +48,14 @@ enum {
   ATTN_ERR_ALIAS = -7,    /* o or lse overlaps an input, or lse overlaps o      */
   ATTN_ERR_HIP = -8,      /* the kernel launch failed (hipGetLastError)         */
   ATTN_ERR_FLAGS = -9,    /* attn_fwd_ex: unknown bits in flags                 */
-  ATTN_ERR_LAYOUT = -10   /* attn_fwd_ex: a stride is negative, not a multiple
+  ATTN_ERR_LAYOUT = -10,  /* attn_fwd_ex: a stride is negative, not a multiple
                              of 8 elements, or rows of a head overlap           */
+  ATTN_ERR_SPLITS = -11,  /* attn_fwd_splitkv: splits not in 1..ATTN_MAX_SPLITS */
+  ATTN_ERR_WORKSPACE = -12 /* attn_fwd_splitkv: workspace_bytes too small       */
 };
+
+/* Largest split count of attn_fwd_splitkv. */
+#define ATTN_MAX_SPLITS 64
 
 /* Largest sequence length accepted: per-head byte offsets and buffer sizes
  * are 32-bit in-kernel (N * 2d bytes must stay below 2^31). */
@@ -129,6 +135,37 @@ typedef struct attn_fwd_args {
  * only.  args == NULL returns ATTN_ERR_NULLPTR.
  */
 int attn_fwd_ex(const attn_fwd_args_t* args);
+
+/*
+ * attn_fwd_splitkv - the same result as attn_fwd_ex, with each head's keys
+ * split into up to `splits` contiguous ranges handled by separate blocks.
+ *
+ * For shapes whose B*H*ceil(N/256) query blocks leave compute units idle
+ * (few heads, long sequences), this multiplies the parallelism.  Each split
+ * s computes a normalised partial output O_s and log-sum-exp lse_s over its
+ * keys; a second kernel merges them exactly, lse = ln sum_s exp(lse_s) and
+ * O = sum_s exp(lse_s - lse) O_s: the combination of per-block row maxima
+ * and sums that page 3 section 1.1 describes, using the log-sum-exp that
+ * page 3 section 5 stores.  Keys are cut at multiples of 64; the split count
+ * actually used is the number of non-empty ranges (at most `splits`).
+ *
+ * args      : as for attn_fwd_ex; flags must not contain ATTN_CAUSAL
+ *             (ATTN_ERR_FLAGS).
+ * splits    : 1 .. ATTN_MAX_SPLITS (ATTN_ERR_SPLITS otherwise).
+ * workspace : device memory of the current device, 16-byte aligned, at least
+ *             attn_fwd_splitkv_workspace(B, H, N, d, splits) bytes, owned by
+ *             the caller and not overlapping any tensor (ATTN_ERR_NULLPTR,
+ *             ATTN_ERR_ALIGN, ATTN_ERR_WORKSPACE, ATTN_ERR_ALIAS).  It holds
+ *             fp32 partial results between the two kernels, both queued on
+ *             args->stream; calls that share a workspace must be ordered.
+ * Returns the codes of attn_fwd_ex plus those above.
+ */
+int attn_fwd_splitkv(const attn_fwd_args_t* args, int splits, void* workspace,
+                     size_t workspace_bytes);
+
+/* Bytes of workspace attn_fwd_splitkv needs (splits_used * B*H*N * (d + 1)
+ * * 4), or 0 for empty or invalid sizes. */
+size_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d, int splits);
 
 /* Static text for a return code (never NULL). */
 const char* attn_strerror(int code);

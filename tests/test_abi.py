@@ -189,3 +189,50 @@ def test_ex_strided_alias_uses_the_strided_extent(lib):
 def test_ex_head_bytes_limit(lib):
     # a head's rows must be addressable with 32-bit byte offsets in the kernels
     assert call_ex(lib, N=1 << 20, ks=(0, 0, 2048), d=64) == SHAPE
+
+
+# ---------------------------------------------------------------------------
+# attn_fwd_splitkv: argument checks and workspace sizing
+# ---------------------------------------------------------------------------
+
+SPLITS, WORKSPACE = -11, -12
+W = 0x40000000  # fake, 16-byte aligned workspace address far from the tensors
+
+
+def call_split(lib, splits=4, ws=W, ws_bytes=1 << 30, **kw):
+    from attention_attn_fwd_07_amd import _Args
+    lib.attn_fwd_splitkv.argtypes = [ctypes.POINTER(_Args), ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_size_t]
+    lib.attn_fwd_splitkv.restype = ctypes.c_int
+    return lib.attn_fwd_splitkv(ctypes.byref(ex_args(**kw)), splits, ws, ws_bytes)
+
+
+def ws_size(lib, B, H, N, d, splits):
+    lib.attn_fwd_splitkv_workspace.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+    lib.attn_fwd_splitkv_workspace.restype = ctypes.c_size_t
+    return lib.attn_fwd_splitkv_workspace(B, H, N, d, splits)
+
+
+@pytest.mark.parametrize("B,H,N,d,splits,used", [
+    (1, 8, 65536, 64, 4, 4), (2, 3, 1000, 128, 7, 6),   # 16 tiles: 3 per split -> 6 splits
+    (1, 1, 100, 64, 8, 2), (1, 1, 64, 128, 5, 1), (4, 2, 129, 64, 64, 3)])
+def test_workspace_size_counts_non_empty_splits(lib, B, H, N, d, splits, used):
+    assert ws_size(lib, B, H, N, d, splits) == used * B * H * N * (d + 1) * 4
+
+
+@pytest.mark.parametrize("args", [(1, 1, 0, 64, 2), (1, 1, 10, 64, 0), (1, 1, 10, 64, 65),
+                                  (1, 1, 10, 96, 2), (-1, 1, 10, 64, 2)])
+def test_workspace_size_zero_for_invalid(lib, args):
+    assert ws_size(lib, *args) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(splits=0), SPLITS), (dict(splits=65), SPLITS), (dict(splits=-2), SPLITS),
+    (dict(flags=1), FLAGS),
+    (dict(ws=None), NULLPTR), (dict(ws=W + 4), ALIGN),
+    (dict(ws_bytes=4 * 2 * 128 * 65 * 2 - 4), WORKSPACE),  # 2 tiles -> 2 splits used
+    (dict(ws=O), ALIAS), (dict(ws=L - 1024 * 16), ALIAS), (dict(ws=Q + 64), ALIAS),
+    (dict(N=0), OK), (dict(N=0, ws=None), OK),
+])
+def test_splitkv_rejects_before_any_hip_call(lib, kw, code):
+    assert call_split(lib, **kw) == code

@@ -35,7 +35,7 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "workload_inputs", "TORCH_DTYPE"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_grad", "workload_inputs", "TORCH_DTYPE"]
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -156,3 +156,14 @@ def workload_inputs(key: int, seed: int | None = None):
     w = WORKLOADS[key]
     return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.key if seed is None else seed,
                     w.mult, w.hot_frac, w.hot_mult)
+
+
+def make_grad(B: int, H: int, N: int, d: int, dtype: str, seed: int):
+    """A seeded upstream gradient dO of shape [B, H, N, d]: standard normal
+    from its own generator (seed offset so it never repeats Q/K/V's stream),
+    rounded to ``dtype`` as in ``make_qkv``."""
+    if dtype not in TORCH_DTYPE:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.Generator(np.random.PCG64(seed + 0x5EED_0000))
+    g = rng.standard_normal((B, H, N, d))
+    return torch.from_numpy(g.astype(np.float32)).to(TORCH_DTYPE[dtype]).contiguous()

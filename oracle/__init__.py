@@ -14,6 +14,9 @@ Modules
 ``online``     the online-softmax recurrence the pages derive (running max m,
                running exp-sum l, rescaled accumulator), in fp64, used only to
                pin "one pass equals two passes" on the oracle itself.
+``backward``   the gradients dQ, dK, dV of the plain definition by the chain
+               rule (the backward that page 3 section 6's autograd wrapper
+               calls), in fp64.
 
 Every function here is pinned by ``tests/test_oracle.py`` against hand-derived
 values (``tests/golden/``), closed forms, brute force and invariants; no
@@ -21,5 +24,7 @@ function here is "parity unpinned".
 """
 from .definition import attention, attention_rows, softmax_probs, scores
 from .online import attention_online
+from .backward import attention_backward
 
-__all__ = ["attention", "attention_rows", "softmax_probs", "scores", "attention_online"]
+__all__ = ["attention", "attention_rows", "softmax_probs", "scores", "attention_online",
+           "attention_backward"]

@@ -56,3 +56,11 @@ def test_workload_table():
     assert w[4].mult == 0.5 and w[5].hot_keys == 655
     assert w[3].scale == float(np.float32(1 / math.sqrt(128)))
     assert w[3].flops == 4 * 2 * 16 * 4096 ** 2 * 128
+
+
+def test_make_grad_is_seeded_and_independent_of_qkv():
+    g1 = datagen.make_grad(1, 2, 33, 64, "bf16", seed=5)
+    g2 = datagen.make_grad(1, 2, 33, 64, "bf16", seed=5)
+    q, k, v = datagen.make_qkv(1, 2, 33, 64, "bf16", seed=5)
+    assert torch.equal(g1, g2) and g1.dtype == torch.bfloat16 and g1.is_contiguous()
+    assert not torch.equal(g1, q) and not torch.equal(g1, v)

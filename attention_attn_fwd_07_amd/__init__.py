@@ -10,6 +10,7 @@ GPU is present, calls raise.
     attn_fwd(q, k, v, o, lse, scale)       # caller-owned outputs, async launch
     p = plan(q, k, v, o, lse, scale); p()  # checked once, then relaunched cheaply
     o, lse = fwd_splitkv(q, k, v, splits=8)  # keys split over 8 blocks, then merged
+    dq, dk, dv = bwd(q, k, v, o, lse, do)    # gradients (include/attn_bwd.h)
 
 Tensors are ``[B, H, N, d]`` fp32/fp16/bf16 with d in {64, 128}; the head
 dimension must be contiguous, the other three dimensions may have any strides
@@ -29,11 +30,23 @@ import os
 from .build import LIB
 
 __all__ = ["attn_fwd", "fwd", "plan", "Plan", "attn_strerror", "attn_version", "library_path",
-           "AttnError", "ATTN_CAUSAL", "splitkv_workspace_size", "fwd_splitkv"]
+           "AttnError", "ATTN_CAUSAL", "splitkv_workspace_size", "fwd_splitkv", "attn_bwd",
+           "bwd", "bwd_workspace_size"]
 
 ATTN_OK = 0
 ATTN_ERR_HIP = -8
 ATTN_CAUSAL = 1
+
+
+class _BwdArgs(ctypes.Structure):
+    """attn_bwd_args_t of include/attn_bwd.h."""
+
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+                ("flags", ctypes.c_uint), ("stream", ctypes.c_void_p)]
 
 
 class _Args(ctypes.Structure):
@@ -83,6 +96,10 @@ def _load():
     lib.attn_fwd_splitkv.restype = ctypes.c_int
     lib.attn_fwd_splitkv_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.attn_fwd_splitkv_workspace.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [ctypes.POINTER(_BwdArgs), vp, ctypes.c_size_t]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace.argtypes = [i64, i64, i64, i64]
+    lib.attn_bwd_workspace.restype = ctypes.c_size_t
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -272,3 +289,60 @@ def fwd(q, k, v, scale: float | None = None, return_lse: bool = True, causal: bo
            if return_lse else None)
     attn_fwd(q, k, v, o, lse, scale, causal=causal)
     return o, lse
+
+
+def bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    """Bytes of workspace ``attn_bwd`` needs (0 for empty sizes)."""
+    return int(_load().attn_bwd_workspace(B, H, N, d))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, workspace, stream=None,
+             causal: bool = False) -> None:
+    """dQ, dK, dV of O = softmax(scale Q K^T) V into the caller's ``dq``, ``dk``,
+    ``dv`` (contiguous [B, H, N, d], bf16 or fp16), given the forward's ``o``
+    and ``lse`` and the upstream gradient ``dout``.  Asynchronous on ``stream``."""
+    torch = _torch()
+    code = _check(q, k, v, o, lse)
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if not isinstance(t, torch.Tensor) or t.device != q.device:
+            raise ValueError(f"{name} must be a tensor on q's device")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q's shape and dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous for the backward")
+    if lse is None:
+        raise ValueError("the backward needs the forward's lse")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    a = _BwdArgs()
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    a.dout, a.lse = dout.data_ptr(), lse.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.B, a.H, a.N, a.d = (int(x) for x in q.shape)
+    a.scale = float(scale)
+    a.dtype = code
+    a.flags = ATTN_CAUSAL if causal else 0
+    a.stream = stream
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wptr = workspace.data_ptr() if workspace is not None else None
+    with torch.cuda.device(q.device):
+        rc = _load().attn_bwd(ctypes.byref(a), ctypes.c_void_p(wptr), nbytes)
+    if rc != ATTN_OK:
+        _raise_for(rc)
+
+
+def bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False):
+    """Allocate dq, dk, dv and the workspace, run ``attn_bwd``, return the grads."""
+    torch = _torch()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    B, H, N, d = (int(x) for x in q.shape)
+    nbytes = bwd_workspace_size(B, H, N, d)
+    ws = torch.empty(max(4, nbytes) // 4, dtype=torch.float32, device=q.device)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, ws, causal=causal)
+    return dq, dk, dv

@@ -1,5 +1,9 @@
 """Build the HIP library ``libattn_fwd.so`` in-tree for gfx950.
 
+Sources: ``csrc/attn_fwd.hip`` (forward, split-KV, C ABI of include/attn_fwd.h)
+and ``csrc/attn_bwd.hip`` (backward, include/attn_bwd.h), both including the
+internal ``csrc/attn_common.h``.
+
 Usage: ``python -m attention_attn_fwd_07_amd.build`` (or ``build()``).  The
 library is compiled with hipcc, for gfx950 only, with packed-fp32 VALU ops
 disabled (the compiler otherwise forms v_pk_* fp32 instructions by itself).
@@ -13,7 +17,8 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SRC = os.path.join(PKG_DIR, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG_DIR, "csrc", "attn_fwd.hip"),
+        os.path.join(PKG_DIR, "csrc", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libattn_fwd.so")
 ARCH = "gfx950"
@@ -29,7 +34,7 @@ def hipcc() -> str:
 def command(out: str = LIB) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            f"-I{INCLUDE}", SRC, "-o", out]
+            f"-I{INCLUDE}", *SRCS, "-o", out]
 
 
 def build(verbose: bool = False) -> str:

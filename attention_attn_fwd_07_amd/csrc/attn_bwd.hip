@@ -1,0 +1,487 @@
+// attn_bwd.hip - attention backward for AMD MI355X (gfx950): dQ, dK, dV of
+// O = softmax(scale * Q K^T) V, from the forward's saved O and log-sum-exp.
+//
+// The gradients are those of the plain definition by the chain rule (the
+// backward that page 3 "OpenAI Triton from introduction to model practice",
+// section 6, calls from its autograd wrapper, which saves q, k, v, o and lse):
+//   P  = exp(s - lse)            s = scale * q.k, recomputed tile by tile
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale * dS K,  dK = scale * dS^T Q.
+// Like the forward, nothing of size N x N reaches device memory: each block
+// recomputes its tiles of s and P from Q, K and the stored lse.
+//
+// Three kernels:
+//   * delta:  D = rowsum(dO * O) per query row, into the workspace;
+//   * dq:     one block = 128 query rows; it loops over key tiles and
+//             accumulates dQ^T = K^T dS^T in registers (the forward's layout:
+//             lane l owns query row l % 32 of its wave);
+//   * dkdv:   one block = 128 keys; it loops over query tiles and accumulates
+//             dK^T = Q^T dS and dV^T = dO^T P (the transposed layout: lane l
+//             owns key l % 32 of its wave).
+// Each gradient row is owned by exactly one lane pair, so there are no
+// atomics and the results are deterministic.
+//
+// MFMA shapes and fragments (v_mfma_f32_32x32x16_{bf16,f16}): the A operand
+// of lane l holds row l % 32, contraction slots 8 (l / 32) .. +7; B holds
+// column l % 32 of the same slots; C holds column l % 32 and rows
+// 8 (r / 4) + 4 (l / 32) + r % 4.  Any consistent assignment of contraction
+// indices to (half, slot) is valid, so a C fragment in register order is
+// directly the B operand of the next product, and the matching A operand is
+// read from a row-major LDS tile with the transposing ds_read_b64_tr_b16.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "attn_bwd.h"
+#include "attn_common.h"
+
+namespace {
+
+// One 64-row tile of a [N, D] tensor in LDS, rows dense (2D bytes), 16-byte
+// chunks XOR-swizzled with swz_k (conflict-free for row reads by 32 lanes of
+// distinct rows).
+template <int D>
+struct Tile {
+  static constexpr int ROWB = D * 2;
+  const lds_u8* base;
+  // A operand: 8 elements of row `row`, contraction slots d = 16 ks + 8 hh ..
+  __device__ __forceinline__ u32x4 row_op(int row, int ks) const {
+    const int hh = (threadIdx.x & 63) >> 5;
+    return *(const lds_u32x4*)(base + row * ROWB + (((2 * ks + hh) ^ swz_k<D>(row)) << 4));
+  }
+  // A operand of a transposed product: column 32 db + l % 32 of rows
+  // r0 + 8 (t / 4) + 4 hh + t % 4, t = 0..7 (the C-fragment row order of
+  // rows r0 .. r0 + 15 in the lane's half).
+  __device__ __forceinline__ u32x4 tr_op(int r0, int db) const {
+    const int lane = threadIdx.x & 63;
+    const int hh = lane >> 5, p16 = lane & 15, colhalf = (lane >> 4) & 1;
+    const int ra = r0 + 4 * hh + (p16 >> 2), rb = ra + 8;
+    const int chunk = 4 * db + 2 * colhalf + ((p16 & 3) >> 1);
+    const int half8 = (p16 & 1) * 8;
+    const lds_u8* a0 = base + ra * ROWB + ((chunk ^ swz_k<D>(ra)) << 4) + half8;
+    const lds_u8* a1 = base + rb * ROWB + ((chunk ^ swz_k<D>(rb)) << 4) + half8;
+    const u32x2 lo =
+        __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
+    const u32x2 hi =
+        __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1)));
+    return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
+// 8 consecutive elements of row `row` (the B operand of a product with a
+// resident row): d = 16 ks + 8 hh .. +7, for ks = 0 .. D/16 - 1.
+template <int D>
+__device__ __forceinline__ void load_row_frag(const uint16_t* __restrict__ X, int row, int N,
+                                              u32x4 (&f)[D / 16]) {
+  const int hh = (threadIdx.x & 63) >> 5;
+  if (row < N) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(X + (size_t)row * D + 8 * hh);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) f[ks] = p[2 * ks];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) f[ks] = (u32x4){0u, 0u, 0u, 0u};
+  }
+}
+
+// Store of one gradient row owned by the lane (C fragments of X^T in
+// register order: columns 32 db + 8 g + 4 hh .. +3), times `mul`, rounded to
+// the element type.
+template <class E, int D>
+__device__ __forceinline__ void store_grad_row(uint16_t* __restrict__ X, int row,
+                                               const f32x16 (&acc)[D / 32], float mul) {
+  const int hh = (threadIdx.x & 63) >> 5;
+  uint16_t* p = X + (size_t)row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x2 w = (u32x2){E::pack2(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul),
+                              E::pack2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      *reinterpret_cast<u32x2*>(p + 32 * db + 8 * g + 4 * hh) = w;
+    }
+}
+
+// Pack a 32 x 32 block of fp32 values in C-fragment order (two 16-row halves
+// hq) as two B operands, rounding to nearest even.
+template <class E>
+__device__ __forceinline__ void pack_frag(const f32x16& x, u32x4 (&pb)[2]) {
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    const int b0 = 8 * hq;
+    pb[hq] = (u32x4){E::pack2(x[b0 + 0], x[b0 + 1]), E::pack2(x[b0 + 2], x[b0 + 3]),
+                     E::pack2(x[b0 + 4], x[b0 + 5]), E::pack2(x[b0 + 6], x[b0 + 7])};
+  }
+}
+
+constexpr int kBN = 64;  // rows per streamed tile (keys in dq, queries in dkdv)
+
+// Query tile of a dq block: for causal attention the tiles of a head are
+// taken last first, so that the blocks with the most key tiles start first.
+template <bool CAUSAL>
+__device__ __forceinline__ int query_tile_b(int t, int nqt) {
+  return CAUSAL ? nqt - 1 - t : t;
+}
+constexpr int kBM = 128; // rows owned per block (queries in dq, keys in dkdv)
+
+// --- D = rowsum(dO * O) ------------------------------------------------------
+// Eight elements (one 16-byte chunk) of a row, widened to fp32 exactly.
+template <class E>
+struct Widen;
+template <>
+struct Widen<Bf16T> {
+  static __device__ __forceinline__ void get(u32x4 x, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(x[i] << 16);
+      f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct Widen<F16T> {
+  static __device__ __forceinline__ void get(u32x4 x, float (&f)[8]) {
+    const f16x8 h = __builtin_bit_cast(f16x8, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
+  }
+};
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta(const uint16_t* __restrict__ O,
+                                                      const uint16_t* __restrict__ dO,
+                                                      float* __restrict__ delta, int rows) {
+  const int r = blockIdx.x * 256 + (int)threadIdx.x;
+  if (r >= rows) return;
+  const u32x4* po = reinterpret_cast<const u32x4*>(O + (size_t)r * D);
+  const u32x4* pd = reinterpret_cast<const u32x4*>(dO + (size_t)r * D);
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < D / 8; ++c) {
+    float a[8], b[8];
+    Widen<E>::get(po[c], a);
+    Widen<E>::get(pd[c], b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(a[i], b[i], acc);
+  }
+  delta[r] = acc;
+}
+
+// --- dQ ------------------------------------------------------------------------
+//
+// Block: 4 waves, query rows qt*128 + 32 w + (l % 32).  Per 64-key tile (K_j,
+// V_j double-buffered in LDS through direct loads):
+//   S^T = K Q^T and dP^T = V dO^T  (A from K / V rows, B = resident Q / dO),
+//   P = 2^(S c2 - lse log2 e), dS = P (dP - D) per element (lane = query),
+//   dQ^T += K^T dS^T               (A from K transposed, B = dS packed).
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                 const float* __restrict__ LSE, const float* __restrict__ delta,
+                 uint16_t* __restrict__ dQ, int N, int nqt, float c2, float scale) {
+  using G = Geo16<D, 4>;
+  constexpr int TB = G::TILEB, KS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
+  lds_u8* const lsm = (lds_u8*)smem;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hh = lane >> 5;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / nqt, qt = query_tile_b<CAUSAL>(tile - bh * nqt, nqt);
+  const size_t hoff = (size_t)bh * N * D;
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + hoff);
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
+  const int q0 = qt * kBM;
+  const int T = ((CAUSAL ? min(N, q0 + kBM) : N) + kBN - 1) / kBN;
+
+  const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(wave), D * 2, D * 2);
+  auto load = [&](int t, int buf) __attribute__((always_inline)) {
+    loader.load(Kb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf) * TB);
+    loader.load(Vb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf + 1) * TB);
+  };
+  load(0, 0);
+
+  const int qrow = q0 + wave * 32 + li;
+  u32x4 qf[KS], df[KS];
+  load_row_frag<D>(Q + hoff, qrow, N, qf);
+  load_row_frag<D>(dO + hoff, qrow, N, df);
+  const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dl = qrow < N ? delta[(size_t)bh * N + qrow] : 0.f;
+  const int lim = CAUSAL ? min(N - 1, qrow) : N - 1;         // last key this row sees
+  const int wlim = CAUSAL ? min(N - 1, q0 + wave * 32) : N - 1;  // smallest over the wave
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
+  wait_vmcnt<0>();
+  // The compiler cannot see the DMA loads (inline asm); using the row
+  // fragments here retires their loads in its bookkeeping, so that it places
+  // no wait of its own inside the loop, where tile loads are in flight.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) __asm__ volatile("" ::"v"(qf[ks]), "v"(df[ks]));
+  __asm__ volatile("" ::"v"(lse2), "v"(dl));
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < T) load(t + 1, buf ^ 1);
+    const Tile<D> kt{lsm + (2 * buf) * TB}, vt{lsm + (2 * buf + 1) * TB};
+    const int j0 = t * kBN;
+    const bool partial = j0 + kBN - 1 > wlim;
+    // one 32-key half of the tile at a time (fewer live registers)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = E::mfma(kt.row_op(32 * sb + li, ks), qf[ks], s);
+        dp = E::mfma(vt.row_op(32 * sb + li, ks), df[ks], dp);
+      }
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(s[r], c2, -lse2));
+        if (partial && j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) > lim) p = 0.f;
+        ds[r] = p * (dp[r] - dl);
+      }
+      u32x4 pb[2];
+      pack_frag<E>(ds, pb);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq)
+          acc[db] = E::mfma(kt.tr_op(32 * sb + 16 * hq, db), pb[hq], acc[db]);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  if (qrow < N) store_grad_row<E, D>(dQ + hoff, qrow, acc, scale);
+}
+
+// --- dK, dV ------------------------------------------------------------------
+//
+// Block: 4 waves, keys kt*128 + 32 w + (l % 32).  Per 64-query tile (Q_i, dO_i
+// double-buffered in LDS, with lse and D of those queries):
+//   S = Q K^T and dP = dO V^T      (A from Q / dO rows, B = resident K / V),
+//   P = 2^(S c2 - lse log2 e), dS = P (dP - D) per element (lane = key),
+//   dV^T += dO^T P, dK^T += Q^T dS (A from dO / Q transposed, B = P / dS).
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                   const float* __restrict__ LSE, const float* __restrict__ delta,
+                   uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nkt,
+                   float c2, float scale) {
+  using G = Geo16<D, 4>;
+  constexpr int TB = G::TILEB, KS = D / 16, DB = D / 32;
+  // two buffers of (Q tile, dO tile), then two buffers of (lse * log2 e, D)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB + 2 * 2 * kBN * 4];
+  lds_u8* const lsm = (lds_u8*)smem;
+  float* const stat = reinterpret_cast<float*>(smem + 4 * TB);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hh = lane >> 5;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / nkt, kt = tile - bh * nkt;
+  const size_t hoff = (size_t)bh * N * D;
+  const unsigned char* Qb = reinterpret_cast<const unsigned char*>(Q + hoff);
+  const unsigned char* dOb = reinterpret_cast<const unsigned char*>(dO + hoff);
+  const int k0 = kt * kBM;
+  // causal: queries before the block's first key see none of its keys
+  const int t0 = CAUSAL ? k0 / kBN : 0;
+  const int T = (N + kBN - 1) / kBN;
+
+  const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(wave), D * 2, D * 2);
+  auto load = [&](int t, int buf) __attribute__((always_inline)) {
+    loader.load(Qb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf) * TB);
+    loader.load(dOb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf + 1) * TB);
+  };
+  // lse (log2 domain; +inf past N, so P = 0) and D of the tile's queries:
+  // thread i < 128 fetches one value into a register early in an iteration
+  // and stores it to LDS at its end, once the iteration's compute is issued.
+  auto fetch_stat = [&](int t) __attribute__((always_inline)) -> float {
+    const int i = threadIdx.x;
+    const int q = t * kBN + (i & (kBN - 1));
+    if (i >= 2 * kBN || q >= N) return i < kBN ? INFINITY : 0.f;
+    return i < kBN ? LSE[(size_t)bh * N + q] * kLog2e : delta[(size_t)bh * N + q];
+  };
+  auto store_stat = [&](float x, int buf) __attribute__((always_inline)) {
+    if (threadIdx.x < 2 * kBN) stat[buf * 2 * kBN + threadIdx.x] = x;
+  };
+  load(t0, 0);
+  store_stat(fetch_stat(t0), 0);
+
+  const int key = k0 + wave * 32 + li;
+  u32x4 kf[KS], vf[KS];
+  load_row_frag<D>(K + hoff, key, N, kf);
+  load_row_frag<D>(V + hoff, key, N, vf);
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = (f32x16){};
+    dv[db] = (f32x16){};
+  }
+  // causal: tiles starting before the wave's last key hold queries that some
+  // of its keys do not see (queries past N have lse = +inf, hence P = 0)
+  const int kmax = k0 + wave * 32 + 31;
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) __asm__ volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
+  __syncthreads();
+
+  for (int t = t0; t < T; ++t) {
+    const int buf = (t - t0) & 1;
+    const bool more = t + 1 < T;
+    float nxt = 0.f;
+    if (more) {
+      nxt = fetch_stat(t + 1);
+      load(t + 1, buf ^ 1);
+    }
+    const Tile<D> qt_{lsm + (2 * buf) * TB}, dot{lsm + (2 * buf + 1) * TB};
+    const float* st = stat + buf * 2 * kBN;
+    const int i0 = t * kBN;
+    const bool partial = CAUSAL && i0 < kmax;
+    // one 32-query half of the tile at a time (fewer live registers)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = E::mfma(qt_.row_op(32 * sb + li, ks), kf[ks], s);
+        dp = E::mfma(dot.row_op(32 * sb + li, ks), vf[ks], dp);
+      }
+      f32x16 p, ds;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // queries 32 sb + 8 g + 4 hh .. +3 of the tile: their lse and D
+        const int qi = 32 * sb + 8 * g + 4 * hh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + qi);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + kBN + qi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pv = fast_exp2(fmaf(s[r], c2, -l4[e]));
+          if (partial && key > i0 + qi + e) pv = 0.f;
+          p[r] = pv;
+          ds[r] = pv * (dp[r] - d4[e]);
+        }
+      }
+      u32x4 pb[2], dsb[2];
+      pack_frag<E>(p, pb);
+      pack_frag<E>(ds, dsb);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+          dv[db] = E::mfma(dot.tr_op(32 * sb + 16 * hq, db), pb[hq], dv[db]);
+          dk[db] = E::mfma(qt_.tr_op(32 * sb + 16 * hq, db), dsb[hq], dk[db]);
+        }
+    }
+    if (more) store_stat(nxt, buf ^ 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  if (key < N) {
+    store_grad_row<E, D>(dK + hoff, key, dk, scale);
+    store_grad_row<E, D>(dV + hoff, key, dv, 1.0f);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+namespace {
+
+bool mul_ok_b(int64_t a, int64_t b, int64_t* out) {
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool overlap_b(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+template <class E, int D, bool C>
+int launch_bwd(const attn_bwd_args_t& a, float* delta, int64_t bh) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
+  const int64_t rows = bh * a.N;
+  const float c2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((attn_bwd_delta<E, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                     s, static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
+                     delta, (int)rows);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  const int64_t nt = (a.N + kBM - 1) / kBM;
+  const uint16_t *q = static_cast<const uint16_t*>(a.q), *k = static_cast<const uint16_t*>(a.k),
+                 *v = static_cast<const uint16_t*>(a.v),
+                 *dout = static_cast<const uint16_t*>(a.dout);
+  hipLaunchKernelGGL((attn_bwd_dq<E, D, C>), dim3((unsigned)(bh * nt)), dim3(256), 0, s, q, k, v,
+                     dout, a.lse, delta, static_cast<uint16_t*>(a.dq), (int)a.N, (int)nt, c2,
+                     a.scale);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  hipLaunchKernelGGL((attn_bwd_dkdv<E, D, C>), dim3((unsigned)(bh * nt)), dim3(256), 0, s, q, k,
+                     v, dout, a.lse, delta, static_cast<uint16_t*>(a.dk),
+                     static_cast<uint16_t*>(a.dv), (int)a.N, (int)nt, c2, a.scale);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+template <class E>
+int launch_bwd_e(const attn_bwd_args_t& a, float* delta, int64_t bh) {
+  const bool c = (a.flags & ATTN_CAUSAL) != 0;
+  if (a.d == 128) return c ? launch_bwd<E, 128, true>(a, delta, bh)
+                           : launch_bwd<E, 128, false>(a, delta, bh);
+  return c ? launch_bwd<E, 64, true>(a, delta, bh) : launch_bwd<E, 64, false>(a, delta, bh);
+}
+
+}  // namespace
+
+extern "C" size_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 0;
+  int64_t bh = 0, bhn = 0;
+  if (!mul_ok_b(B, H, &bh) || !mul_ok_b(bh, N, &bhn) || bhn > INT64_MAX / 4) return 0;
+  return (size_t)bhn * 4;
+}
+
+extern "C" int attn_bwd(const attn_bwd_args_t* args, void* ws, size_t ws_bytes) {
+  // --- validation: no HIP call before this block has passed -------------
+  if (args == nullptr) return ATTN_ERR_NULLPTR;
+  const attn_bwd_args_t& a = *args;
+  const int64_t B = a.B, H = a.H, N = a.N, d = a.d;
+  if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
+  if (a.dtype != ATTN_DTYPE_F16 && a.dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!isfinite(a.scale)) return ATTN_ERR_SCALE;
+  if ((a.flags & ~ATTN_CAUSAL) != 0) return ATTN_ERR_FLAGS;
+  int64_t bh = 0, bhn = 0, elems = 0;
+  if (!mul_ok_b(B, H, &bh) || !mul_ok_b(bh, N, &bhn) || !mul_ok_b(bhn, d, &elems) ||
+      elems > INT64_MAX / 2)
+    return ATTN_ERR_SHAPE;
+  if (bhn == 0) return ATTN_OK;
+  if (N > ATTN_MAX_N || N * d * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  if (bh * ((N + kBM - 1) / kBM) > INT32_MAX || bhn > INT32_MAX) return ATTN_ERR_SHAPE;
+  const void* ptrs[9] = {a.q, a.k, a.v, a.o, a.dout, a.lse, a.dq, a.dk, a.dv};
+  for (const void* p : ptrs)
+    if (p == nullptr) return ATTN_ERR_NULLPTR;
+  if (ws == nullptr) return ATTN_ERR_NULLPTR;
+  for (int i = 0; i < 9; ++i)
+    if ((reinterpret_cast<uintptr_t>(ptrs[i]) & (i == 5 ? 3u : 15u)) != 0) return ATTN_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return ATTN_ERR_ALIGN;
+  const size_t tb = (size_t)elems * 2, lb = (size_t)bhn * 4;
+  if (ws_bytes < lb) return ATTN_ERR_WORKSPACE;
+  const size_t sizes[9] = {tb, tb, tb, tb, tb, lb, tb, tb, tb};
+  // outputs (dq, dk, dv) and the workspace must not overlap anything else
+  for (int i = 6; i < 9; ++i)
+    for (int j = 0; j < 9; ++j)
+      if (j != i && overlap_b(ptrs[i], sizes[i], ptrs[j], sizes[j])) return ATTN_ERR_ALIAS;
+  for (int j = 0; j < 9; ++j)
+    if (overlap_b(ws, lb, ptrs[j], sizes[j])) return ATTN_ERR_ALIAS;
+
+  // --- launch -------------------------------------------------------------
+  float* delta = static_cast<float*>(ws);
+  if (a.dtype == ATTN_DTYPE_BF16) return launch_bwd_e<Bf16T>(a, delta, bh);
+  return launch_bwd_e<F16T>(a, delta, bh);
+}

@@ -41,13 +41,18 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of MI355X bf16 MFMA peak"
-KERNEL_SRC = os.path.join(ROOT, "attention_attn_fwd_07_amd", "csrc", "attn_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "attention_attn_fwd_07_amd", "csrc", f)
+               for f in ("attn_fwd.hip", "attn_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernels' sources (the code the profiles describe)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(w) -> int:

@@ -236,3 +236,77 @@ def test_workspace_size_zero_for_invalid(lib, args):
 ])
 def test_splitkv_rejects_before_any_hip_call(lib, kw, code):
     assert call_split(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# attn_bwd: argument checks
+# ---------------------------------------------------------------------------
+
+DQ, DK, DV, DO, LS = 0x600000, 0x700000, 0x800000, 0x900000, 0xA00000
+
+
+def bwd_args(q=Q, k=K, v=V, o=O, dout=DO, lse=LS, dq=DQ, dk=DK, dv=DV, B=1, H=2, N=128, d=64,
+             scale=0.125, dtype=BF16, flags=0):
+    from attention_attn_fwd_07_amd import _BwdArgs
+    a = _BwdArgs()
+    a.q, a.k, a.v, a.o, a.dout, a.lse, a.dq, a.dk, a.dv = q, k, v, o, dout, lse, dq, dk, dv
+    a.B, a.H, a.N, a.d, a.scale, a.dtype, a.flags = B, H, N, d, scale, dtype, flags
+    a.stream = None
+    return a
+
+
+def call_bwd(lib, ws=W, ws_bytes=1 << 20, **kw):
+    from attention_attn_fwd_07_amd import _BwdArgs
+    lib.attn_bwd.argtypes = [ctypes.POINTER(_BwdArgs), ctypes.c_void_p, ctypes.c_size_t]
+    lib.attn_bwd.restype = ctypes.c_int
+    return lib.attn_bwd(ctypes.byref(bwd_args(**kw)), ws, ws_bytes)
+
+
+def test_bwd_args_struct_matches_the_header(tmp_path):
+    import shutil
+    import subprocess
+    from attention_attn_fwd_07_amd import _BwdArgs
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in _BwdArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "attn_bwd.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(attn_bwd_args_t));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(attn_bwd_args_t, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(_BwdArgs)
+    assert got[1:] == [getattr(_BwdArgs, f).offset for f in fields]
+
+
+def test_bwd_workspace_size(lib):
+    lib.attn_bwd_workspace.argtypes = [ctypes.c_int64] * 4
+    lib.attn_bwd_workspace.restype = ctypes.c_size_t
+    assert lib.attn_bwd_workspace(2, 3, 100, 64) == 2 * 3 * 100 * 4
+    assert lib.attn_bwd_workspace(2, 3, 100, 96) == 0
+    assert lib.attn_bwd_workspace(0, 3, 100, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=F32), DTYPE), (dict(dtype=5), DTYPE), (dict(d=96), HEAD_DIM),
+    (dict(scale=float("nan")), SCALE), (dict(flags=4), FLAGS), (dict(N=-1), SHAPE),
+    (dict(dq=None), NULLPTR), (dict(lse=None), NULLPTR), (dict(dout=None), NULLPTR),
+    (dict(ws=None), NULLPTR), (dict(dk=DK + 8), ALIGN), (dict(lse=LS + 2), ALIGN),
+    (dict(ws=W + 4), ALIGN), (dict(ws_bytes=2 * 128 * 4 - 4), WORKSPACE),
+    (dict(dq=Q), ALIAS), (dict(dv=DK + 64), ALIAS), (dict(dk=LS), ALIAS),
+    (dict(ws=DV + 128), ALIAS), (dict(ws=LS), ALIAS),
+    (dict(N=0), OK), (dict(N=0, dq=None, ws=None), OK),
+])
+def test_bwd_rejects_before_any_hip_call(lib, kw, code):
+    assert call_bwd(lib, **kw) == code
+
+
+def test_bwd_null_args(lib):
+    lib.attn_bwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+    lib.attn_bwd.restype = ctypes.c_int
+    assert lib.attn_bwd(None, W, 1 << 20) == NULLPTR

@@ -136,6 +136,13 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
+    ap.add_argument("--causal", action="store_true",
+                    help="causal variant (flops counted over the N(N+1)/2 visible pairs)")
+    ap.add_argument("--splitkv", type=int, default=0, metavar="S",
+                    help="forward through attn_fwd_splitkv with S key splits (+ merge)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (dQ, dK, dV) instead of the forward; "
+                         "flops counted as 10 B H N^2 d (the five products)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -166,7 +173,35 @@ def main(argv=None) -> int:
 
     # One checked plan: the timed loop only relaunches it, so host-side Python
     # work stays far below a kernel's duration and the GPU never waits on it.
-    launch = attn.plan(qd, kd, vd, o, lse, w.scale, stream)
+    mode = "fwd"
+    pairs = w.N * w.N if not args.causal else w.N * (w.N + 1) // 2  # visible (i, j)
+    flops = 4 * w.B * w.H * pairs * w.d
+    if args.backward:
+        if w.dtype == "f32":
+            print("bench.py: the backward takes bf16/fp16 only", file=sys.stderr)
+            return 2
+        attn.fwd(qd, kd, vd, w.scale, causal=args.causal)  # warm the forward once
+        o, lse = attn.fwd(qd, kd, vd, w.scale, causal=args.causal)
+        g = datagen.make_grad(w.B, w.H, w.N, w.d, w.dtype, seed=w.key).to(dev)
+        grads = [torch.empty_like(qd) for _ in range(3)]
+        ws = torch.empty(attn.bwd_workspace_size(w.B, w.H, w.N, w.d) // 4, dtype=torch.float32,
+                         device=dev)
+
+        def launch():
+            attn.attn_bwd(qd, kd, vd, o, lse, g, *grads, w.scale, ws, stream,
+                          causal=args.causal)
+        flops = 10 * w.B * w.H * pairs * w.d
+        mode = "bwd"
+    elif args.splitkv:
+        ws = torch.empty(attn.splitkv_workspace_size(w.B, w.H, w.N, w.d, args.splitkv) // 4,
+                         dtype=torch.float32, device=dev)
+        launch = attn.plan(qd, kd, vd, o, lse, w.scale, stream, splits=args.splitkv,
+                           workspace=ws)
+        mode = f"fwd split-KV S={args.splitkv}"
+    else:
+        launch = attn.plan(qd, kd, vd, o, lse, w.scale, stream, causal=args.causal)
+    if args.causal:
+        mode += " causal"
     for _ in range(args.warmup):
         launch()
     K = args.steps
@@ -183,8 +218,8 @@ def main(argv=None) -> int:
 
     kern_ms = ev0.elapsed_time(ev1) / K  # HIP events on the launch stream, K launches
     ms_per_step = wall * 1e3 / K
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (kern_ms * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
     line = {
@@ -200,17 +235,19 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": w.describe(),
+        "config": dict(w.describe(), mode=mode, causal=bool(args.causal)),
         "pct_of_peak": round(100.0 * value / peak, 2),
         "kernel_ms": {"mean": round(kern_ms, 5)},
-        "hbm_gbps_algorithmic": round(algorithmic_bytes(w) / (kern_ms * 1e-3) / 1e9, 1),
+        "hbm_gbps_algorithmic": (round(algorithmic_bytes(w) / (kern_ms * 1e-3) / 1e9, 1)
+                                 if not args.backward else None),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_for(w)},
+                     "traffic": traffic_for(w) if mode == "fwd" else None},
         "kernel_sha256_16": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        if mode == "fwd":
+            line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
     print(json.dumps(line), flush=True)
     return 0
 

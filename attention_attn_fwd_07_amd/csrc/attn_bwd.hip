@@ -118,12 +118,6 @@ __device__ __forceinline__ void pack_frag(const f32x16& x, u32x4 (&pb)[2]) {
 
 constexpr int kBN = 64;  // rows per streamed tile (keys in dq, queries in dkdv)
 
-// Query tile of a dq block: for causal attention the tiles of a head are
-// taken last first, so that the blocks with the most key tiles start first.
-template <bool CAUSAL>
-__device__ __forceinline__ int query_tile_b(int t, int nqt) {
-  return CAUSAL ? nqt - 1 - t : t;
-}
 constexpr int kBM = 128; // rows owned per block (queries in dq, keys in dkdv)
 
 // --- D = rowsum(dO * O) ------------------------------------------------------
@@ -189,8 +183,10 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hh = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / nqt, qt = query_tile_b<CAUSAL>(tile - bh * nqt, nqt);
+  // causal: the last query tile of a head visits the most key tiles
+  WorkItem wi = work_item<CAUSAL>(blockIdx.x, gridDim.x, nqt);
+  if (CAUSAL) wi.t = nqt - 1 - wi.t;
+  const int bh = wi.bh, qt = wi.t;
   const size_t hoff = (size_t)bh * N * D;
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + hoff);
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
@@ -282,8 +278,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(const uint16_t* __restrict_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hh = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / nkt, kt = tile - bh * nkt;
+  // causal: the first key tile of a head is seen by the most query tiles
+  const WorkItem wi = work_item<CAUSAL>(blockIdx.x, gridDim.x, nkt);
+  const int bh = wi.bh, kt = wi.t;
   const size_t hoff = (size_t)bh * N * D;
   const unsigned char* Qb = reinterpret_cast<const unsigned char*>(Q + hoff);
   const unsigned char* dOb = reinterpret_cast<const unsigned char*>(dO + hoff);

@@ -68,6 +68,28 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return x * q + (x < r ? x : r) + i;
 }
 
+// Work item (head bh, tile t) of block b in a grid of nbh heads x nt tiles.
+// Equal-length tiles: the xcd_remap order (a head's tiles contiguous on one
+// XCD).  Tiles whose length grows or shrinks with t (causal attention):
+// level by level over all heads, so that every head's longest tiles start
+// before any shorter one (longest-processing-time order keeps the CUs evenly
+// loaded to the end of the grid); level 0 is t = 0 and the caller maps it to
+// its longest tile.  The hardware deals blocks round-robin over the XCDs, so
+// when nbh is a multiple of 8 a head's blocks all land on XCD bh % 8 and
+// still share its L2.
+struct WorkItem {
+  int bh, t;
+};
+template <bool BY_LEVEL>
+__device__ __forceinline__ WorkItem work_item(int b, int nb, int nt) {
+  if (BY_LEVEL) {
+    const int nbh = nb / nt;
+    return {b % nbh, b / nbh};
+  }
+  const int tile = xcd_remap(b, nb);
+  return {tile / nt, tile - (tile / nt) * nt};
+}
+
 // Value held by lane l ^ 32, combined with the lane's own by op.
 __device__ __forceinline__ float xhalf_max(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

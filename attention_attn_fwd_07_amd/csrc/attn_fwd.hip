@@ -155,11 +155,14 @@ __device__ __forceinline__ int key_tiles(int N, int q0, int bm, int bn) {
   return (nk + bn - 1) / bn;
 }
 
-// Query tile of a block: for causal attention the tiles of a head are taken
-// last first, so that the blocks with the most key tiles start first.
+// (head, query tile) of a block.  For causal attention the last query tile
+// of a head visits the most key tiles, so level 0 of the by-level order is
+// the last tile.
 template <bool CAUSAL>
-__device__ __forceinline__ int query_tile(int t, int nqt) {
-  return CAUSAL ? nqt - 1 - t : t;
+__device__ __forceinline__ WorkItem query_item(int nqt) {
+  WorkItem w = work_item<CAUSAL>(blockIdx.x, gridDim.x, nqt);
+  if (CAUSAL) w.t = nqt - 1 - w.t;
+  return w;
 }
 
 // Keys past the lane's limit in a partial tile: a value that cannot win the
@@ -289,8 +292,8 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hh = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
+  const WorkItem wi = query_item<CAUSAL>(nqt);
+  const int bh = wi.bh, qt = wi.t;
   const uint16_t* const Qh = Q + L.base(L.q, bh);
   uint16_t* const Oh = O + L.base(L.o, bh);
   // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
@@ -574,8 +577,8 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int grp = wave >> 2;
   const int li = lane & 31, hh = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
+  const WorkItem wi = query_item<CAUSAL>(nqt);
+  const int bh = wi.bh, qt = wi.t;
   const uint16_t* const Qh = Q + L.base(L.q, bh);
   uint16_t* const Oh = O + L.base(L.o, bh);
   // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
@@ -760,8 +763,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hh = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / nqt, qt = query_tile<CAUSAL>(tile - bh * nqt, nqt);
+  const WorkItem wi = query_item<CAUSAL>(nqt);
+  const int bh = wi.bh, qt = wi.t;
   const float* Qh = Q + L.base(L.q, bh);
   // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
   const int kb0 = sp.first_key(), Nk = sp.keys(N);

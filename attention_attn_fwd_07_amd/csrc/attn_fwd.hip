@@ -214,7 +214,8 @@ __device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float 
   // Eight independent partial sums: a single running sum would be a chain
   // of 32 dependent adds, whose latency nothing hides when one wave of the
   // SIMD is in its softmax phase.
-  float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // The first eight probabilities start the partial sums (no adds to zero).
+  float part[8];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     float p[16];
@@ -222,7 +223,10 @@ __device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float 
     for (int r = 0; r < 16; ++r) {
       p[r] = fast_exp2(fmaf(s[sb][r], c2, -m));
       if (TAIL && (j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) > lim)) p[r] = 0.f;
-      part[r & 7] += p[r];
+      if (sb == 0 && r < 8)
+        part[r] = p[r];
+      else
+        part[r & 7] += p[r];
     }
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
@@ -1012,21 +1016,24 @@ int launch(void (*kernel)(const T*, const T*, const T*, T*, float*, int, int, fl
 
 constexpr int kNumCUs = 256;  // MI355X
 
-// Kernel choice for the 16-bit types: the 8-wave ping-pong kernel (256 query
-// rows per block) when it still gives every CU a block, else the 4-wave
-// pipelined kernel (128 rows per block, up to two blocks per CU).  The
+// Kernel choice for the 16-bit types: at d = 128 the 8-wave ping-pong kernel
+// (256 query rows per block) when it still gives every CU a block, else the
+// 4-wave pipelined kernel (128 rows per block, up to two blocks per CU).  At
+// d = 64 the pipelined kernel throughout: there the softmax work per tile is
+// as large as the MFMA work, and the pipelined kernel's two blocks per CU
+// measured 2-8 % faster than the ping-pong kernel on long sequences.  The
 // environment variable ATTN_FWD_KERNEL=pingpong|pipelined forces one (for
 // tests and sweeps).
-bool use_pingpong(int64_t blocks256) {
+bool use_pingpong(int64_t blocks256, int64_t d) {
   const char* env = getenv("ATTN_FWD_KERNEL");
   if (env != nullptr && strcmp(env, "pingpong") == 0) return true;
   if (env != nullptr && strcmp(env, "pipelined") == 0) return false;
-  return blocks256 >= kNumCUs;
+  return d == 128 && blocks256 >= kNumCUs;
 }
 
 template <class E, class T, bool C>
 int launch16(const Launch& a) {
-  if (use_pingpong(a.bh * ((a.N + 255) / 256) * a.splits)) {
+  if (use_pingpong(a.bh * ((a.N + 255) / 256) * a.splits, a.d)) {
     const int64_t nqt = (a.N + 255) / 256;
     auto kern = a.d == 128 ? attn_fwd_pp16<E, 128, C> : attn_fwd_pp16<E, 64, C>;
     return launch<T>(kern, a.bh * nqt, kPPThreads, (int)nqt, a);

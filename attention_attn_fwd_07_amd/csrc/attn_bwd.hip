@@ -39,29 +39,48 @@
 
 namespace {
 
-// One 64-row tile of a [N, D] tensor in LDS, rows dense (2D bytes), 16-byte
-// chunks XOR-swizzled with swz_k (conflict-free for row reads by 32 lanes of
-// distinct rows).
+// Per-lane parts of the fragment addresses in a [rows, D] LDS tile whose
+// rows are dense (2D bytes) with 16-byte chunks XOR-swizzled by swz_k
+// (conflict-free for row reads by 32 lanes of distinct rows).  swz_k depends
+// on row bits 0-3 only, and the loop indices only set chunk-index bits that
+// the lane's own chunk bits XOR with, so the read of row block r0 (a
+// multiple of 16) at k-step ks (column block db) is at
+//   r0 * 2D + (lane offset ^ (ks << 5))      ( ^ (db << 6) )
+// with the row block in the instruction's immediate offset: a handful of
+// per-lane registers instead of one per distinct read.
+template <int D>
+struct FragOff {
+  static constexpr int ROWB = D * 2;
+  uint32_t row;       // A operand rows: row l % 32 of the block, chunk l / 32
+  uint32_t tra, trb;  // transposed reads: rows 4 (l / 32) + (l % 16) / 4 and that + 8
+  __device__ __forceinline__ FragOff() {
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 31, hh = lane >> 5, p16 = lane & 15, colhalf = (lane >> 4) & 1;
+    row = (uint32_t)(li * ROWB + ((hh ^ swz_k<D>(li)) << 4));
+    const int ra = 4 * hh + (p16 >> 2), rb = ra + 8;
+    const int c0 = 2 * colhalf + ((p16 & 3) >> 1);  // chunk within column block 0
+    const int half8 = (p16 & 1) * 8;
+    tra = (uint32_t)(ra * ROWB + ((c0 ^ swz_k<D>(ra)) << 4) + half8);
+    trb = (uint32_t)(rb * ROWB + ((c0 ^ swz_k<D>(rb)) << 4) + half8);
+  }
+};
+
+// One tile of a [N, D] tensor in LDS (layout above).
 template <int D>
 struct Tile {
   static constexpr int ROWB = D * 2;
   const lds_u8* base;
-  // A operand: 8 elements of row `row`, contraction slots d = 16 ks + 8 hh ..
-  __device__ __forceinline__ u32x4 row_op(int row, int ks) const {
-    const int hh = (threadIdx.x & 63) >> 5;
-    return *(const lds_u32x4*)(base + row * ROWB + (((2 * ks + hh) ^ swz_k<D>(row)) << 4));
+  // A operand: 8 elements of row r0 + l % 32, contraction slots
+  // d = 16 ks + 8 (l / 32) .. +7.
+  __device__ __forceinline__ u32x4 row_op(const FragOff<D>& f, int r0, int ks) const {
+    return *(const lds_u32x4*)(base + r0 * ROWB + (f.row ^ (uint32_t)(ks << 5)));
   }
   // A operand of a transposed product: column 32 db + l % 32 of rows
   // r0 + 8 (t / 4) + 4 hh + t % 4, t = 0..7 (the C-fragment row order of
   // rows r0 .. r0 + 15 in the lane's half).
-  __device__ __forceinline__ u32x4 tr_op(int r0, int db) const {
-    const int lane = threadIdx.x & 63;
-    const int hh = lane >> 5, p16 = lane & 15, colhalf = (lane >> 4) & 1;
-    const int ra = r0 + 4 * hh + (p16 >> 2), rb = ra + 8;
-    const int chunk = 4 * db + 2 * colhalf + ((p16 & 3) >> 1);
-    const int half8 = (p16 & 1) * 8;
-    const lds_u8* a0 = base + ra * ROWB + ((chunk ^ swz_k<D>(ra)) << 4) + half8;
-    const lds_u8* a1 = base + rb * ROWB + ((chunk ^ swz_k<D>(rb)) << 4) + half8;
+  __device__ __forceinline__ u32x4 tr_op(const FragOff<D>& f, int r0, int db) const {
+    const lds_u8* a0 = base + r0 * ROWB + (f.tra ^ (uint32_t)(db << 6));
+    const lds_u8* a1 = base + r0 * ROWB + (f.trb ^ (uint32_t)(db << 6));
     const u32x2 lo =
         __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0)));
     const u32x2 hi =
@@ -220,6 +239,7 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __asm__ volatile("" ::"v"(lse2), "v"(dl));
   __syncthreads();
 
+  const FragOff<D> fo;
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
     if (t + 1 < T) load(t + 1, buf ^ 1);
@@ -232,8 +252,8 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = E::mfma(kt.row_op(32 * sb + li, ks), qf[ks], s);
-        dp = E::mfma(vt.row_op(32 * sb + li, ks), df[ks], dp);
+        s = E::mfma(kt.row_op(fo, 32 * sb, ks), qf[ks], s);
+        dp = E::mfma(vt.row_op(fo, 32 * sb, ks), df[ks], dp);
       }
       f32x16 ds;
 #pragma unroll
@@ -248,7 +268,7 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq)
-          acc[db] = E::mfma(kt.tr_op(32 * sb + 16 * hq, db), pb[hq], acc[db]);
+          acc[db] = E::mfma(kt.tr_op(fo, 32 * sb + 16 * hq, db), pb[hq], acc[db]);
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -258,23 +278,33 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
 // --- dK, dV ------------------------------------------------------------------
 //
-// Block: 4 waves, keys kt*128 + 32 w + (l % 32).  Per 64-query tile (Q_i, dO_i
-// double-buffered in LDS, with lse and D of those queries):
-//   S = Q K^T and dP = dO V^T      (A from Q / dO rows, B = resident K / V),
+// Block: 8 waves, keys kt*256 + 32 w + (l % 32).  K rows stay in registers
+// (the B operand of S); the block's V rows are staged once in LDS and read
+// back as the B operand of dP, which keeps a wave at no more than 256 VGPRs
+// (two waves per SIMD, one block per CU): the resident state is K (D/4
+// VGPRs) and the fp32 dK, dV accumulators (D/2 each).  Per 64-query tile
+// (Q_i, dO_i double-buffered in LDS, with lse and D of those queries):
+//   S = Q K^T and dP = dO V^T      (A from Q / dO rows),
 //   P = 2^(S c2 - lse log2 e), dS = P (dP - D) per element (lane = key),
 //   dV^T += dO^T P, dK^T += Q^T dS (A from dO / Q transposed, B = P / dS).
+constexpr int kKW = 8;             // waves of a dK/dV block
+constexpr int kBK = 32 * kKW;      // keys per dK/dV block
+
 template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(64 * kKW) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const float* __restrict__ LSE, const float* __restrict__ delta,
                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nkt,
                    float c2, float scale) {
-  using G = Geo16<D, 4>;
+  using G = Geo16<D, kKW>;
   constexpr int TB = G::TILEB, KS = D / 16, DB = D / 32;
-  // two buffers of (Q tile, dO tile), then two buffers of (lse * log2 e, D)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB + 2 * 2 * kBN * 4];
+  constexpr int VT = kBK / kBN;  // V tiles of the block
+  // two buffers of (Q tile, dO tile), the block's V rows, then two buffers
+  // of (lse * log2 e, D)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[(4 + VT) * TB + 2 * 2 * kBN * 4];
   lds_u8* const lsm = (lds_u8*)smem;
-  float* const stat = reinterpret_cast<float*>(smem + 4 * TB);
+  float* const stat = reinterpret_cast<float*>(smem + (4 + VT) * TB);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hh = lane >> 5;
 
@@ -284,16 +314,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(const uint16_t* __restrict_
   const size_t hoff = (size_t)bh * N * D;
   const unsigned char* Qb = reinterpret_cast<const unsigned char*>(Q + hoff);
   const unsigned char* dOb = reinterpret_cast<const unsigned char*>(dO + hoff);
-  const int k0 = kt * kBM;
+  const int k0 = kt * kBK;
   // causal: queries before the block's first key see none of its keys
   const int t0 = CAUSAL ? k0 / kBN : 0;
   const int T = (N + kBN - 1) / kBN;
 
-  const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(wave), D * 2, D * 2);
+  const TileLoader<D, kKW> loader(__builtin_amdgcn_readfirstlane(wave), D * 2, D * 2);
   auto load = [&](int t, int buf) __attribute__((always_inline)) {
     loader.load(Qb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf) * TB);
     loader.load(dOb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf + 1) * TB);
   };
+  // The block's V rows (tiles past N are left unwritten: they only feed
+  // the gradients of keys past N, which are not stored).
+  const Tile<D> vt{lsm + 4 * TB};
+  {
+    const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
+#pragma unroll
+    for (int u = 0; u < VT; ++u)
+      if (k0 + u * kBN < N) loader.load(Vb, loader.koff, loader.krs, k0 + u * kBN, N, lsm + (4 + u) * TB);
+  }
   // lse (log2 domain; +inf past N, so P = 0) and D of the tile's queries:
   // thread i < 128 fetches one value into a register early in an iteration
   // and stores it to LDS at its end, once the iteration's compute is issued.
@@ -310,9 +349,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(const uint16_t* __restrict_
   store_stat(fetch_stat(t0), 0);
 
   const int key = k0 + wave * 32 + li;
-  u32x4 kf[KS], vf[KS];
+  u32x4 kf[KS];
   load_row_frag<D>(K + hoff, key, N, kf);
-  load_row_frag<D>(V + hoff, key, N, vf);
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -324,9 +362,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(const uint16_t* __restrict_
   const int kmax = k0 + wave * 32 + 31;
   wait_vmcnt<0>();
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) __asm__ volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
+  for (int ks = 0; ks < KS; ++ks) __asm__ volatile("" ::"v"(kf[ks]));
   __syncthreads();
 
+  const FragOff<D> fo;
   for (int t = t0; t < T; ++t) {
     const int buf = (t - t0) & 1;
     const bool more = t + 1 < T;
@@ -345,10 +384,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(const uint16_t* __restrict_
       f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = E::mfma(qt_.row_op(32 * sb + li, ks), kf[ks], s);
-        dp = E::mfma(dot.row_op(32 * sb + li, ks), vf[ks], dp);
+        s = E::mfma(qt_.row_op(fo, 32 * sb, ks), kf[ks], s);
+        dp = E::mfma(dot.row_op(fo, 32 * sb, ks), vt.row_op(fo, 32 * wave, ks), dp);
       }
-      f32x16 p, ds;
+      __builtin_amdgcn_sched_barrier(0);
+      // P and dS in place of S and dP
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // queries 32 sb + 8 g + 4 hh .. +3 of the tile: their lse and D
@@ -360,20 +400,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv(const uint16_t* __restrict_
           const int r = 4 * g + e;
           float pv = fast_exp2(fmaf(s[r], c2, -l4[e]));
           if (partial && key > i0 + qi + e) pv = 0.f;
-          p[r] = pv;
-          ds[r] = pv * (dp[r] - d4[e]);
+          s[r] = pv;
+          dp[r] = pv * (dp[r] - d4[e]);
         }
       }
       u32x4 pb[2], dsb[2];
-      pack_frag<E>(p, pb);
-      pack_frag<E>(ds, dsb);
+      pack_frag<E>(s, pb);
+      pack_frag<E>(dp, dsb);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {
-          dv[db] = E::mfma(dot.tr_op(32 * sb + 16 * hq, db), pb[hq], dv[db]);
-          dk[db] = E::mfma(qt_.tr_op(32 * sb + 16 * hq, db), dsb[hq], dk[db]);
+          dv[db] = E::mfma(dot.tr_op(fo, 32 * sb + 16 * hq, db), pb[hq], dv[db]);
+          dk[db] = E::mfma(qt_.tr_op(fo, 32 * sb + 16 * hq, db), dsb[hq], dk[db]);
         }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more) store_stat(nxt, buf ^ 1);
     wait_vmcnt<0>();
@@ -420,9 +462,10 @@ int launch_bwd(const attn_bwd_args_t& a, float* delta, int64_t bh) {
                      dout, a.lse, delta, static_cast<uint16_t*>(a.dq), (int)a.N, (int)nt, c2,
                      a.scale);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
-  hipLaunchKernelGGL((attn_bwd_dkdv<E, D, C>), dim3((unsigned)(bh * nt)), dim3(256), 0, s, q, k,
-                     v, dout, a.lse, delta, static_cast<uint16_t*>(a.dk),
-                     static_cast<uint16_t*>(a.dv), (int)a.N, (int)nt, c2, a.scale);
+  const int64_t nkt = (a.N + kBK - 1) / kBK;
+  hipLaunchKernelGGL((attn_bwd_dkdv<E, D, C>), dim3((unsigned)(bh * nkt)), dim3(64 * kKW), 0, s,
+                     q, k, v, dout, a.lse, delta, static_cast<uint16_t*>(a.dk),
+                     static_cast<uint16_t*>(a.dv), (int)a.N, (int)nkt, c2, a.scale);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -191,18 +191,40 @@ __device__ __forceinline__ float tile_max16(const f32x16 (&s)[2], float c2) {
 // same reference.
 constexpr float kRescaleThreshold = 8.0f;
 
+// Move each row's reference to max(m, m_tile) and rescale its l and
+// accumulator by 2^(m_old - m_new) (1 for rows whose reference stays).
+template <int D>
+__device__ __forceinline__ void rescale_to(float m_tile, float& m, float& l,
+                                           f32x16 (&acc)[Geo16<D>::DB]) {
+  const float m_new = fmaxf(m, m_tile);
+  const float alpha = fast_exp2(m - m_new);
+  m = m_new;
+  l *= alpha;
+#pragma unroll
+  for (int db = 0; db < Geo16<D>::DB; ++db) acc[db] *= alpha;
+}
+
 template <int D>
 __device__ __forceinline__ void maybe_rescale(float m_tile, float& m, float& l,
                                               f32x16 (&acc)[Geo16<D>::DB]) {
-  if (__builtin_amdgcn_ballot_w64(m_tile > m + kRescaleThreshold) != 0) {  // wave-uniform
-    const float m_new = fmaxf(m, m_tile);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < Geo16<D>::DB; ++db) acc[db] *= alpha;
-  }
+  if (__builtin_amdgcn_ballot_w64(m_tile > m + kRescaleThreshold) != 0)  // wave-uniform
+    rescale_to<D>(m_tile, m, l, acc);
 }
+
+// Sum test, the cheaper alternative to the max test (used by the ping-pong
+// kernel without a causal mask): P is first formed against the current reference m, without the
+// tile's row max.  If every lane's sum of its 32 probabilities is at most
+// 2^8, every P is at most 2^8 - the max test's bound - and the tile is done.
+// Otherwise the row max is taken, the rows are rescaled and P is formed
+// again.  The rare path runs whenever the max test would (and also for some
+// tiles whose max exceeds m by 3 to 8 doublings).  The limit is kept low on
+// purpose: a key that dominates its row then almost always moves the
+// reference to its own score, so its P is exactly 1 and loses nothing to the
+// 16-bit rounding of P; with a limit of 2^12 the rounding of such P (up to
+// 2^-9 relative for bf16) measurably raised the worst-case output error on
+// rows dominated by a few large scores.  The first tile always sets m from
+// its row max.
+constexpr float kSumLimit = 256.0f;
 
 // P = 2^(s * c2 - m), packed to the element type (RNE) as the B operand of
 // the P.V product; returns this lane's fp32 row-sum contribution (the
@@ -341,6 +363,9 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   float m = tile_max16(sA, c2);  // the first tile sets the reference exactly
   block_barrier();               // kbuf0 is free for K_2 only after every wave read K_0
 
+  // This kernel keeps the max test: the sum test's branch would split the
+  // block in which the compiler interleaves a tile's softmax with the next
+  // tile's MFMAs (measured slower here).
   auto body = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], const lds_u8* kb_next,
                   const lds_u8* vb_cur, lds_u8* kb_load, lds_u8* vb_load) {
     const int j1 = (t + 1) * G::BN;
@@ -491,6 +516,24 @@ __device__ __forceinline__ void mfma_phase(const lds_u8* lsm, uint32_t kbo, uint
   }
   __builtin_amdgcn_sched_group_barrier(MFMA, LA, 0);
   __builtin_amdgcn_s_setprio(0);
+}
+
+// S = K Q^T over one 64-key K tile (LDS byte offset kbo) alone: the rare
+// path of the sum test forms S again rather than keeping it live.
+template <class E, int D>
+__device__ __forceinline__ void qk_tile(const lds_u8* lsm, uint32_t kbo, LdsLanes<D> ln,
+                                        const u32x4 (&qf)[Geo16<D>::KS], f32x16 (&s)[2]) {
+  using G = Geo16<D>;
+  const uint32_t kqb = ln.kq + kbo;
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) {
+    const lds_u8* ka = lsm + (kqb ^ (uint32_t)(ks << 5));
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+      s[sb] = E::mfma(*(const lds_u32x4*)(ka + sb * 32 * G::ROWB), qf[ks], s[sb]);
+  }
 }
 
 // Tile loads of the ping-pong kernel, issued by the four waves of one group.
@@ -662,18 +705,54 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     mfma_phase<E, D>(lsm, kbo, vbo, ln, t > 0, pb, acc, qf, sc);
   };
   // VALU phase of tile t.
-  auto valu_full = [&]() __attribute__((always_inline)) {
-    maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
-    l += softmax16<E, false>(sc, m, c2, pb, 0, 0);
+  // The rare path forms S again from K_t, which stays in its ring slot until
+  // both groups have finished the VALU phase of tile t.
+  // The causal kernel keeps the max test: its extra masking code leaves no
+  // registers for the sum test's second pass.
+  auto valu_full = [&](int t) __attribute__((always_inline)) {
+    if (CAUSAL) {
+      maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
+      l += softmax16<E, false>(sc, m, c2, pb, 0, 0);
+      return;
+    }
+    float ps = softmax16<E, false>(sc, m, c2, pb, 0, 0);
+    if (__builtin_amdgcn_ballot_w64(ps > kSumLimit) != 0) {  // rare; wave-uniform
+      qk_tile<E, D>(lsm, (uint32_t)(t % kRing) * TB, ln, qf, sc);
+      rescale_to<D>(tile_max16(sc, c2), m, l, acc);
+      ps = softmax16<E, false>(sc, m, c2, pb, 0, 0);
+    }
+    l += ps;
+  };
+  // The first tile sets the reference from its row max (m = -inf before).
+  auto valu_first = [&]() __attribute__((always_inline)) {
+    if (kl.partial(0, G::BN)) {
+      mask_tail16(sc, 0, kl.lane_lim, c2);
+      rescale_to<D>(tile_max16(sc, c2), m, l, acc);
+      l += softmax16<E, true>(sc, m, c2, pb, 0, kl.lane_lim);
+    } else {
+      rescale_to<D>(tile_max16(sc, c2), m, l, acc);
+      l += softmax16<E, false>(sc, m, c2, pb, 0, 0);
+    }
   };
   auto valu_any = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * G::BN;
     if (kl.partial(j0, G::BN)) {
-      mask_tail16(sc, j0, kl.lane_lim, c2);
-      maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
-      l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+      if (CAUSAL) {
+        mask_tail16(sc, j0, kl.lane_lim, c2);
+        maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
+        l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+        return;
+      }
+      float ps = softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+      if (__builtin_amdgcn_ballot_w64(ps > kSumLimit) != 0) {
+        qk_tile<E, D>(lsm, (uint32_t)(t % kRing) * TB, ln, qf, sc);
+        mask_tail16(sc, j0, kl.lane_lim, c2);
+        rescale_to<D>(tile_max16(sc, c2), m, l, acc);
+        ps = softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+      }
+      l += ps;
     } else {
-      valu_full();
+      valu_full(t);
     }
   };
   // Tiles between the first and the last: all full without a causal mask;
@@ -682,7 +761,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (CAUSAL)
       valu_any(t);
     else
-      valu_full();
+      valu_full(t);
   };
   auto pv_last = [&]() __attribute__((always_inline)) {
     uint32_t vq = ln.vq;
@@ -697,7 +776,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // slot 2t: MFMA phase of tile t, load V_{t+2}; slot 2t+1: VALU phase of
     // tile t, await V_t.
     block_barrier(); mfma_tile(0); if (2 < T) load_tile(2);
-    block_barrier(); valu_any(0); wait_tile(0);
+    block_barrier(); valu_first(); wait_tile(0);
     for (int t = 1; t < T - 1; ++t) {
       block_barrier(); mfma_tile(t); if (t + 2 < T) load_tile(t + 2);
       block_barrier(); valu_mid(t); wait_tile(t);
@@ -713,7 +792,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // K_{t+1}; slot 2t+2: VALU phase of tile t.
     block_barrier();  // slot 0
     block_barrier(); mfma_tile(0); if (3 < T) load_tile(3); wait_tile(1);
-    block_barrier(); valu_any(0);
+    block_barrier(); valu_first();
     for (int t = 1; t < T - 1; ++t) {
       block_barrier(); mfma_tile(t); if (t + 3 < T) load_tile(t + 3); wait_tile(t + 1);
       block_barrier(); valu_mid(t);

@@ -251,6 +251,25 @@ def test_forced_kernel_hot_keys(kernel, monkeypatch):
 
 
 @pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("direction", [1, -1])
+def test_forced_kernel_moving_max(kernel, d, direction, monkeypatch):
+    """Key rows scaled by a factor that grows (or shrinks) along the sequence,
+    so that every row's running max keeps rising tile after tile (or is set by
+    the first tiles): the rescale paths of both kernels - the max test, and
+    the ping-pong kernel's sum test with its second pass - run many times.
+    The scaled keys are rounded to bf16 before either side reads them."""
+    monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
+    N = 2000
+    q, k, v = datagen.make_qkv(1, 2, N, d, "bf16", seed=57 + d)
+    ramp = torch.linspace(0.25, 6.0, N, dtype=torch.float32)
+    if direction < 0:
+        ramp = ramp.flip(0)
+    k = (k.float() * ramp[None, None, :, None]).to(torch.bfloat16)
+    full_parity(q, k, v, 1.0 / math.sqrt(d), "bf16", f"{kernel} d={d} moving max {direction}")
+
+
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 1.5])
 def test_forced_kernel_scales(kernel, scale, monkeypatch):
     """Negative, zero and large scales on each 16-bit kernel."""

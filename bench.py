@@ -41,6 +41,9 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of MI355X bf16 MFMA peak"
+METRIC_CAUSAL = "attention fwd causal TFLOP/s (4·B·H·d·N(N+1)/2) and % of MI355X bf16 MFMA peak"
+METRIC_BWD = "attention bwd TFLOP/s (10·B·H·N²·d) and % of MI355X bf16 MFMA peak"
+METRIC_BWD_CAUSAL = "attention bwd causal TFLOP/s (10·B·H·d·N(N+1)/2) and % of MI355X bf16 MFMA peak"
 KERNEL_SRCS = [os.path.join(ROOT, "attention_attn_fwd_07_amd", "csrc", f)
                for f in ("attn_fwd.hip", "attn_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -142,7 +145,8 @@ def main(argv=None) -> int:
                     help="forward through attn_fwd_splitkv with S key splits (+ merge)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (dQ, dK, dV) instead of the forward; "
-                         "flops counted as 10 B H N^2 d (the five products)")
+                         "flops counted as 10 B H N^2 d (the five products; N(N+1)/2 pairs "
+                         "in place of N^2 when causal)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -223,7 +227,8 @@ def main(argv=None) -> int:
     peak = PEAK_TFLOPS[w.dtype]
 
     line = {
-        "metric": METRIC,
+        "metric": ((METRIC_BWD_CAUSAL if args.causal else METRIC_BWD) if args.backward
+                   else (METRIC_CAUSAL if args.causal else METRIC)),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

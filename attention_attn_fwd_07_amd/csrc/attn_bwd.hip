@@ -250,11 +250,15 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       f32x16 s = (f32x16){}, dp = (f32x16){};
+      // MFMA sections run at raised priority, so that the SIMD's other wave,
+      // when it is in its exponential section, fills the issue gaps instead.
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = E::mfma(kt.row_op(fo, 32 * sb, ks), qf[ks], s);
         dp = E::mfma(vt.row_op(fo, 32 * sb, ks), df[ks], dp);
       }
+      __builtin_amdgcn_s_setprio(0);
       f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -264,11 +268,13 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
       u32x4 pb[2];
       pack_frag<E>(ds, pb);
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq)
           acc[db] = E::mfma(kt.tr_op(fo, 32 * sb + 16 * hq, db), pb[hq], acc[db]);
+      __builtin_amdgcn_s_setprio(0);
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -382,12 +388,14 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       f32x16 s = (f32x16){}, dp = (f32x16){};
+      __builtin_amdgcn_s_setprio(2);  // MFMA section (see attn_bwd_dq)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = E::mfma(qt_.row_op(fo, 32 * sb, ks), kf[ks], s);
         dp = E::mfma(dot.row_op(fo, 32 * sb, ks), vt.row_op(fo, 32 * wave, ks), dp);
       }
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       // P and dS in place of S and dP
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -408,6 +416,7 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       pack_frag<E>(s, pb);
       pack_frag<E>(dp, dsb);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -416,6 +425,7 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           dk[db] = E::mfma(qt_.tr_op(fo, 32 * sb + 16 * hq, db), dsb[hq], dk[db]);
         }
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
     }
     if (more) store_stat(nxt, buf ^ 1);
     wait_vmcnt<0>();

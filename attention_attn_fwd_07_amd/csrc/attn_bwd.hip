@@ -165,8 +165,8 @@ struct Widen<F16T> {
 template <class E, int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta(const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ delta, int rows) {
-  const int r = blockIdx.x * 256 + (int)threadIdx.x;
+                                                      float* __restrict__ delta, long long rows) {
+  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
   if (r >= rows) return;
   const u32x4* po = reinterpret_cast<const u32x4*>(O + (size_t)r * D);
   const u32x4* pd = reinterpret_cast<const u32x4*>(dO + (size_t)r * D);
@@ -462,7 +462,7 @@ int launch_bwd(const attn_bwd_args_t& a, float* delta, int64_t bh) {
   const float c2 = a.scale * kLog2e;
   hipLaunchKernelGGL((attn_bwd_delta<E, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
                      s, static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                     delta, (int)rows);
+                     delta, (long long)rows);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   const int64_t nt = (a.N + kBM - 1) / kBM;
   const uint16_t *q = static_cast<const uint16_t*>(a.q), *k = static_cast<const uint16_t*>(a.k),

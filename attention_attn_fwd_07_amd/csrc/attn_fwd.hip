@@ -1030,10 +1030,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* __restr
                                                             int nbh, int S, Layout L) {
   constexpr int TPR = D / 4;                // threads per row
   constexpr int RPB = kMergeThreads / TPR;  // rows per block
-  const int r = blockIdx.x * RPB + (int)threadIdx.x / TPR;  // row of the B*H*N rows
+  const long long r = (long long)blockIdx.x * RPB + (int)threadIdx.x / TPR;  // of B*H*N rows
   const int c = 4 * ((int)threadIdx.x % TPR);
-  if (r >= nbh * N) return;
   const size_t plane = (size_t)nbh * N;
+  if (r >= (long long)plane) return;
   float mx = -INFINITY;
   for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, lpart[sp * plane + r]);
   float sum = 0.f;
@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* __restr
   }
   const float inv = 1.0f / sum;
   o[0] *= inv, o[1] *= inv, o[2] *= inv, o[3] *= inv;
-  const int bh = r / N, i = r - bh * N;
+  const int bh = (int)(r / N), i = (int)(r - (long long)bh * N);
   OUT::store4(O + L.base(L.o, bh) + (long long)i * L.o[2] + c, o);
   if (LSE != nullptr && c == 0) LSE[r] = mx + log2f(sum) * kLn2;
 }

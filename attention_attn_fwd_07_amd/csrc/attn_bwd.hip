@@ -39,12 +39,28 @@
 
 namespace {
 
+// LDS swizzle of the backward's tiles: physical 16-byte chunk = logical chunk
+// ^ swz_b(row).  Each tile is read two ways - as A-operand rows (16-byte
+// reads by 16 lanes of 16 consecutive rows) and transposed
+// (ds_read_b64_tr_b16: per 32 lanes, 4 consecutive rows x 4 consecutive
+// chunks) - and swz_b keeps both free of LDS bank conflicts (64 banks of 4
+// bytes): over each aligned group of 16 rows it permutes the chunk positions,
+// and the 4 rows of each aligned group of 4 get distinct values in the chunk
+// bits above the 4 that a transposed read spans (for d = 64, where two rows
+// share the bank range, distinct for rows of the same parity).
+template <int D> __device__ __forceinline__ int swz_b(int row);
+template <> __device__ __forceinline__ int swz_b<128>(int row) {
+  return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+template <> __device__ __forceinline__ int swz_b<64>(int row) {
+  return (((row >> 1) & 1) << 2) ^ ((row >> 2) & 1) ^ (((row >> 3) & 1) << 1);
+}
+
 // Per-lane parts of the fragment addresses in a [rows, D] LDS tile whose
-// rows are dense (2D bytes) with 16-byte chunks XOR-swizzled by swz_k
-// (conflict-free for row reads by 32 lanes of distinct rows).  swz_k depends
-// on row bits 0-3 only, and the loop indices only set chunk-index bits that
-// the lane's own chunk bits XOR with, so the read of row block r0 (a
-// multiple of 16) at k-step ks (column block db) is at
+// rows are dense (2D bytes) with 16-byte chunks XOR-swizzled by swz_b.
+// swz_b depends on row bits 0-3 only, and the loop indices only set
+// chunk-index bits that the lane's own chunk bits XOR with, so the read of
+// row block r0 (a multiple of 16) at k-step ks (column block db) is at
 //   r0 * 2D + (lane offset ^ (ks << 5))      ( ^ (db << 6) )
 // with the row block in the instruction's immediate offset: a handful of
 // per-lane registers instead of one per distinct read.
@@ -56,12 +72,12 @@ struct FragOff {
   __device__ __forceinline__ FragOff() {
     const int lane = threadIdx.x & 63;
     const int li = lane & 31, hh = lane >> 5, p16 = lane & 15, colhalf = (lane >> 4) & 1;
-    row = (uint32_t)(li * ROWB + ((hh ^ swz_k<D>(li)) << 4));
+    row = (uint32_t)(li * ROWB + ((hh ^ swz_b<D>(li)) << 4));
     const int ra = 4 * hh + (p16 >> 2), rb = ra + 8;
     const int c0 = 2 * colhalf + ((p16 & 3) >> 1);  // chunk within column block 0
     const int half8 = (p16 & 1) * 8;
-    tra = (uint32_t)(ra * ROWB + ((c0 ^ swz_k<D>(ra)) << 4) + half8);
-    trb = (uint32_t)(rb * ROWB + ((c0 ^ swz_k<D>(rb)) << 4) + half8);
+    tra = (uint32_t)(ra * ROWB + ((c0 ^ swz_b<D>(ra)) << 4) + half8);
+    trb = (uint32_t)(rb * ROWB + ((c0 ^ swz_b<D>(rb)) << 4) + half8);
   }
 };
 
@@ -162,10 +178,13 @@ struct Widen<F16T> {
   }
 };
 
+// Per query row: (lse * log2 e, D = rowsum(dO * O)), the two statistics both
+// gradient kernels read, as one 8-byte pair (so that one load brings both).
 template <class E, int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta(const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ delta, long long rows) {
+                                                      const float* __restrict__ LSE,
+                                                      float2* __restrict__ stats, long long rows) {
   const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
   if (r >= rows) return;
   const u32x4* po = reinterpret_cast<const u32x4*>(O + (size_t)r * D);
@@ -179,8 +198,38 @@ __global__ __launch_bounds__(256) void attn_bwd_delta(const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = fmaf(a[i], b[i], acc);
   }
-  delta[r] = acc;
+  stats[r] = make_float2(LSE[r] * kLog2e, acc);
 }
+
+// Loads of ROWS rows of a [N, D] tensor (rows 2D bytes apart in memory) into
+// a dense LDS tile in the swz_b layout, by NW waves: 16-byte direct
+// global->LDS loads, one buffer descriptor per tile whose range ends at row
+// N, so rows past N read as zero.
+template <int D, int ROWS, int NW>
+struct RowLoader {
+  static constexpr int ROWB = 2 * D, CH = D / 8;
+  static constexpr int RPL = 1024 / ROWB;     // rows per wave-wide 16-byte load
+  static constexpr int STEP = NW * RPL;       // rows between one wave's loads
+  static constexpr int LOADS = ROWS / STEP;   // loads per wave and tile
+  static_assert(STEP % 16 == 0 && LOADS >= 1 && ROWS % STEP == 0,
+                "the swizzle bits must not depend on the load");
+  uint32_t off;  // this lane's byte offset from the tile's first row
+  int wave;      // index among the NW loading waves (uniform)
+  __device__ __forceinline__ explicit RowLoader(int w) : wave(w) {
+    const int lane = threadIdx.x & 63;
+    const int r0 = wave * RPL + lane / CH, p = lane % CH;
+    off = (uint32_t)(r0 * ROWB + ((p ^ swz_b<D>(r0)) << 4));
+  }
+  // Rows q0 .. q0 + ROWS - 1 (q0 < N).
+  __device__ __forceinline__ void load(const unsigned char* Xb, int q0, int N,
+                                       lds_u8* dst) const {
+    const i32x4 rsrc = buffer_rsrc(Xb + (size_t)q0 * ROWB, (N - q0) * ROWB);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      lds_dma16(rsrc, off + (uint32_t)(u * STEP * ROWB),
+                lds_addr(dst + (u * NW + wave) * 1024));
+  }
+};
 
 // --- dQ ------------------------------------------------------------------------
 //
@@ -193,8 +242,8 @@ template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                 const float* __restrict__ LSE, const float* __restrict__ delta,
-                 uint16_t* __restrict__ dQ, int N, int nqt, float c2, float scale) {
+                 const float2* __restrict__ stats, uint16_t* __restrict__ dQ, int N, int nqt,
+                 float c2, float scale) {
   using G = Geo16<D, 4>;
   constexpr int TB = G::TILEB, KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
@@ -212,10 +261,10 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int q0 = qt * kBM;
   const int T = ((CAUSAL ? min(N, q0 + kBM) : N) + kBN - 1) / kBN;
 
-  const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(wave), D * 2, D * 2);
+  const RowLoader<D, kBN, 4> loader(__builtin_amdgcn_readfirstlane(wave));
   auto load = [&](int t, int buf) __attribute__((always_inline)) {
-    loader.load(Kb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf) * TB);
-    loader.load(Vb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf + 1) * TB);
+    loader.load(Kb, t * kBN, N, lsm + (2 * buf) * TB);
+    loader.load(Vb, t * kBN, N, lsm + (2 * buf + 1) * TB);
   };
   load(0, 0);
 
@@ -223,8 +272,8 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   u32x4 qf[KS], df[KS];
   load_row_frag<D>(Q + hoff, qrow, N, qf);
   load_row_frag<D>(dO + hoff, qrow, N, df);
-  const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dl = qrow < N ? delta[(size_t)bh * N + qrow] : 0.f;
+  const float2 st = qrow < N ? stats[(size_t)bh * N + qrow] : make_float2(INFINITY, 0.f);
+  const float lse2 = st.x, dl = st.y;
   const int lim = CAUSAL ? min(N - 1, qrow) : N - 1;         // last key this row sees
   const int wlim = CAUSAL ? min(N - 1, q0 + wave * 32) : N - 1;  // smallest over the wave
   f32x16 acc[DB];
@@ -300,7 +349,7 @@ template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kKW) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                   const float* __restrict__ LSE, const float* __restrict__ delta,
+                   const float2* __restrict__ stats,
                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nkt,
                    float c2, float scale) {
   using G = Geo16<D, kKW>;
@@ -325,10 +374,10 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int t0 = CAUSAL ? k0 / kBN : 0;
   const int T = (N + kBN - 1) / kBN;
 
-  const TileLoader<D, kKW> loader(__builtin_amdgcn_readfirstlane(wave), D * 2, D * 2);
+  const RowLoader<D, kBN, kKW> loader(__builtin_amdgcn_readfirstlane(wave));
   auto load = [&](int t, int buf) __attribute__((always_inline)) {
-    loader.load(Qb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf) * TB);
-    loader.load(dOb, loader.koff, loader.krs, t * kBN, N, lsm + (2 * buf + 1) * TB);
+    loader.load(Qb, t * kBN, N, lsm + (2 * buf) * TB);
+    loader.load(dOb, t * kBN, N, lsm + (2 * buf + 1) * TB);
   };
   // The block's V rows (tiles past N are left unwritten: they only feed
   // the gradients of keys past N, which are not stored).
@@ -337,7 +386,7 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + hoff);
 #pragma unroll
     for (int u = 0; u < VT; ++u)
-      if (k0 + u * kBN < N) loader.load(Vb, loader.koff, loader.krs, k0 + u * kBN, N, lsm + (4 + u) * TB);
+      if (k0 + u * kBN < N) loader.load(Vb, k0 + u * kBN, N, lsm + (4 + u) * TB);
   }
   // lse (log2 domain; +inf past N, so P = 0) and D of the tile's queries:
   // thread i < 128 fetches one value into a register early in an iteration
@@ -346,7 +395,7 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int i = threadIdx.x;
     const int q = t * kBN + (i & (kBN - 1));
     if (i >= 2 * kBN || q >= N) return i < kBN ? INFINITY : 0.f;
-    return i < kBN ? LSE[(size_t)bh * N + q] * kLog2e : delta[(size_t)bh * N + q];
+    return i < kBN ? stats[(size_t)bh * N + q].x : stats[(size_t)bh * N + q].y;
   };
   auto store_stat = [&](float x, int buf) __attribute__((always_inline)) {
     if (threadIdx.x < 2 * kBN) stat[buf * 2 * kBN + threadIdx.x] = x;
@@ -456,31 +505,30 @@ bool overlap_b(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 template <class E, int D, bool C>
-int launch_bwd(const attn_bwd_args_t& a, float* delta, int64_t bh) {
+int launch_bwd(const attn_bwd_args_t& a, float2* stats, int64_t bh) {
   hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
   const int64_t rows = bh * a.N;
   const float c2 = a.scale * kLog2e;
   hipLaunchKernelGGL((attn_bwd_delta<E, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
                      s, static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                     delta, (long long)rows);
+                     a.lse, stats, (long long)rows);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   const int64_t nt = (a.N + kBM - 1) / kBM;
   const uint16_t *q = static_cast<const uint16_t*>(a.q), *k = static_cast<const uint16_t*>(a.k),
                  *v = static_cast<const uint16_t*>(a.v),
                  *dout = static_cast<const uint16_t*>(a.dout);
   hipLaunchKernelGGL((attn_bwd_dq<E, D, C>), dim3((unsigned)(bh * nt)), dim3(256), 0, s, q, k, v,
-                     dout, a.lse, delta, static_cast<uint16_t*>(a.dq), (int)a.N, (int)nt, c2,
-                     a.scale);
+                     dout, stats, static_cast<uint16_t*>(a.dq), (int)a.N, (int)nt, c2, a.scale);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   const int64_t nkt = (a.N + kBK - 1) / kBK;
   hipLaunchKernelGGL((attn_bwd_dkdv<E, D, C>), dim3((unsigned)(bh * nkt)), dim3(64 * kKW), 0, s,
-                     q, k, v, dout, a.lse, delta, static_cast<uint16_t*>(a.dk),
+                     q, k, v, dout, stats, static_cast<uint16_t*>(a.dk),
                      static_cast<uint16_t*>(a.dv), (int)a.N, (int)nkt, c2, a.scale);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 template <class E>
-int launch_bwd_e(const attn_bwd_args_t& a, float* delta, int64_t bh) {
+int launch_bwd_e(const attn_bwd_args_t& a, float2* delta, int64_t bh) {
   const bool c = (a.flags & ATTN_CAUSAL) != 0;
   if (a.d == 128) return c ? launch_bwd<E, 128, true>(a, delta, bh)
                            : launch_bwd<E, 128, false>(a, delta, bh);
@@ -492,8 +540,8 @@ int launch_bwd_e(const attn_bwd_args_t& a, float* delta, int64_t bh) {
 extern "C" size_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {
   if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 0;
   int64_t bh = 0, bhn = 0;
-  if (!mul_ok_b(B, H, &bh) || !mul_ok_b(bh, N, &bhn) || bhn > INT64_MAX / 4) return 0;
-  return (size_t)bhn * 4;
+  if (!mul_ok_b(B, H, &bh) || !mul_ok_b(bh, N, &bhn) || bhn > INT64_MAX / 8) return 0;
+  return (size_t)bhn * 8;
 }
 
 extern "C" int attn_bwd(const attn_bwd_args_t* args, void* ws, size_t ws_bytes) {
@@ -520,18 +568,18 @@ extern "C" int attn_bwd(const attn_bwd_args_t* args, void* ws, size_t ws_bytes) 
   for (int i = 0; i < 9; ++i)
     if ((reinterpret_cast<uintptr_t>(ptrs[i]) & (i == 5 ? 3u : 15u)) != 0) return ATTN_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return ATTN_ERR_ALIGN;
-  const size_t tb = (size_t)elems * 2, lb = (size_t)bhn * 4;
-  if (ws_bytes < lb) return ATTN_ERR_WORKSPACE;
+  const size_t tb = (size_t)elems * 2, lb = (size_t)bhn * 4, wb = (size_t)bhn * 8;
+  if (ws_bytes < wb) return ATTN_ERR_WORKSPACE;
   const size_t sizes[9] = {tb, tb, tb, tb, tb, lb, tb, tb, tb};
   // outputs (dq, dk, dv) and the workspace must not overlap anything else
   for (int i = 6; i < 9; ++i)
     for (int j = 0; j < 9; ++j)
       if (j != i && overlap_b(ptrs[i], sizes[i], ptrs[j], sizes[j])) return ATTN_ERR_ALIAS;
   for (int j = 0; j < 9; ++j)
-    if (overlap_b(ws, lb, ptrs[j], sizes[j])) return ATTN_ERR_ALIAS;
+    if (overlap_b(ws, wb, ptrs[j], sizes[j])) return ATTN_ERR_ALIAS;
 
   // --- launch -------------------------------------------------------------
-  float* delta = static_cast<float*>(ws);
+  float2* delta = static_cast<float2*>(ws);
   if (a.dtype == ATTN_DTYPE_BF16) return launch_bwd_e<Bf16T>(a, delta, bh);
   return launch_bwd_e<F16T>(a, delta, bh);
 }

@@ -62,14 +62,16 @@ typedef struct attn_bwd_args {
   void* stream;
 } attn_bwd_args_t;
 
-/* Bytes of workspace attn_bwd needs: B*H*N*4 (the per-row D values), 0 for
- * empty or invalid sizes. */
+/* Bytes of workspace attn_bwd needs: B*H*N*8 (per query row the pair
+ * lse * log2(e) and D = rowsum(dO * O), both fp32), 0 for empty or invalid
+ * sizes. */
 size_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d);
 
 /*
  * attn_bwd - dQ, dK, dV (see above).  Three kernels queued on args->stream:
- * D = rowsum(dO * O) into the workspace, then dQ (blocks over query rows)
- * and dK, dV (blocks over keys), with no atomics (deterministic).
+ * the per-row (lse * log2(e), D) pairs into the workspace, then dQ (blocks
+ * over query rows) and dK, dV (blocks over keys), with no atomics
+ * (deterministic).
  *
  * workspace : device memory, 16-byte aligned, at least attn_bwd_workspace()
  *             bytes, not overlapping any tensor; owned by the caller.

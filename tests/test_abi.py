@@ -287,7 +287,7 @@ def test_bwd_args_struct_matches_the_header(tmp_path):
 def test_bwd_workspace_size(lib):
     lib.attn_bwd_workspace.argtypes = [ctypes.c_int64] * 4
     lib.attn_bwd_workspace.restype = ctypes.c_size_t
-    assert lib.attn_bwd_workspace(2, 3, 100, 64) == 2 * 3 * 100 * 4
+    assert lib.attn_bwd_workspace(2, 3, 100, 64) == 2 * 3 * 100 * 8
     assert lib.attn_bwd_workspace(2, 3, 100, 96) == 0
     assert lib.attn_bwd_workspace(0, 3, 100, 64) == 0
 
@@ -297,7 +297,7 @@ def test_bwd_workspace_size(lib):
     (dict(scale=float("nan")), SCALE), (dict(flags=4), FLAGS), (dict(N=-1), SHAPE),
     (dict(dq=None), NULLPTR), (dict(lse=None), NULLPTR), (dict(dout=None), NULLPTR),
     (dict(ws=None), NULLPTR), (dict(dk=DK + 8), ALIGN), (dict(lse=LS + 2), ALIGN),
-    (dict(ws=W + 4), ALIGN), (dict(ws_bytes=2 * 128 * 4 - 4), WORKSPACE),
+    (dict(ws=W + 4), ALIGN), (dict(ws_bytes=2 * 128 * 8 - 4), WORKSPACE),
     (dict(dq=Q), ALIAS), (dict(dv=DK + 64), ALIAS), (dict(dk=LS), ALIAS),
     (dict(ws=DV + 128), ALIAS), (dict(ws=LS), ALIAS),
     (dict(N=0), OK), (dict(N=0, dq=None, ws=None), OK),

@@ -301,22 +301,33 @@ __device__ __forceinline__ void pv16(const lds_u8* vb, const u32x4 (&pb)[2][2],
 // S_{t+1} and, rarely, rescales.  K therefore runs one tile ahead of V:
 // iteration t reads K_{t+1} and V_t while K_{t+2} and V_{t+1} stream into
 // the other K and V buffers.
-template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// KS2 = 2 (small grids): 8 waves, two per 32-row group.  Waves w and w + 4
+// take the same rows and alternate key tiles (even tiles to w, odd tiles to
+// w + 4), each with its own K/V buffers and online-softmax state; at the end
+// the two states are merged through LDS, m = max(m0, m1), acc and l scaled by
+// 2^(m_h - m).  This puts two waves on every SIMD when the grid alone gives
+// one.  Both halves run the same number of local tiles, so their barriers
+// pair up; with an odd tile count the odd half's last local tile lies past
+// the keys, is not loaded, and is fully masked.  Used without a causal mask
+// or a split, for at least two key tiles.
+template <class E, int D, bool CAUSAL, int KS2>
+__global__ __launch_bounds__(kThreads * KS2) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, int N, int nqt, float c2, Layout L, Split sp) {
   using G = Geo16<D, 4>;
   constexpr int BM = 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
-  lds_u8* const lsm = (lds_u8*)smem;
+  static_assert(KS2 == 1 || (KS2 == 2 && !CAUSAL), "the key split is for the plain forward");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB * KS2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int rw = wave & 3, kh = wave >> 2;  // row group, key half
+  const int li = lane & 31, hh = lane >> 5;
+  lds_u8* const lsm = (lds_u8*)smem + kh * 4 * G::TILEB;
   lds_u8* const kbuf0 = lsm;
   lds_u8* const kbuf1 = lsm + G::TILEB;
   lds_u8* const vbuf0 = lsm + 2 * G::TILEB;
   lds_u8* const vbuf1 = lsm + 3 * G::TILEB;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 31, hh = lane >> 5;
 
   const WorkItem wi = query_item<CAUSAL>(nqt);
   const int bh = wi.bh, qt = wi.t;
@@ -329,17 +340,21 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const unsigned char* Vb =
       reinterpret_cast<const unsigned char*>(V + L.base(L.v, bh) + (long long)kb0 * L.v[2]);
 
-  const int ntiles = key_tiles<CAUSAL>(Nk, qt * BM, BM, G::BN);
-  const TileLoader<D, 4> loader(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
-                               (int)(L.k[2] * 2), (int)(L.v[2] * 2));
-  loader.load_k(Kb, 0, Nk, kbuf0);
-  loader.load_v(Vb, 0, Nk, vbuf0);
-  if (ntiles > 1) loader.load_k(Kb, G::BN, Nk, kbuf1);
+  const int T = key_tiles<CAUSAL>(Nk, qt * BM, BM, G::BN);
+  // local tile i of this wave's half is global tile KS2 * i + kh; both halves run ntiles
+  const int ntiles = (T + KS2 - 1) / KS2;
+  auto J = [&](int i) __attribute__((always_inline)) { return (KS2 * i + kh) * G::BN; };
+  const TileLoader<D, 4> loader(rw, (int)(L.k[2] * 2), (int)(L.v[2] * 2));
+  if (J(0) < Nk) {
+    loader.load_k(Kb, J(0), Nk, kbuf0);
+    loader.load_v(Vb, J(0), Nk, vbuf0);
+  }
+  if (ntiles > 1 && J(1) < Nk) loader.load_k(Kb, J(1), Nk, kbuf1);
 
   // Q fragment, resident for the whole key loop: lane (li, hh) holds
   // d = 16 ks + 8 hh + [0, 8) of query row qrow.
-  const int qrow = qt * BM + wave * 32 + li;
-  const KeyLimit<CAUSAL> kl(Nk, qrow, qt * BM + wave * 32);
+  const int qrow = qt * BM + rw * 32 + li;
+  const KeyLimit<CAUSAL> kl(Nk, qrow, qt * BM + rw * 32);
   u32x4 qf[G::KS];
   if (qrow < N) {
     const u32x4* qp = reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * L.q[2] + 8 * hh);
@@ -359,7 +374,7 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   f32x16 sA[2], sB[2];
   qk16<E, D>(kbuf0, qf, sA);
-  if (kl.partial(0, G::BN)) mask_tail16(sA, 0, kl.lane_lim, c2);
+  if (kl.partial(J(0), G::BN)) mask_tail16(sA, J(0), kl.lane_lim, c2);
   float m = tile_max16(sA, c2);  // the first tile sets the reference exactly
   block_barrier();               // kbuf0 is free for K_2 only after every wave read K_0
 
@@ -368,12 +383,12 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // tile's MFMAs (measured slower here).
   auto body = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], const lds_u8* kb_next,
                   const lds_u8* vb_cur, lds_u8* kb_load, lds_u8* vb_load) {
-    const int j1 = (t + 1) * G::BN;
-    if (t + 2 < ntiles) loader.load_k(Kb, j1 + G::BN, Nk, kb_load);
-    loader.load_v(Vb, j1, Nk, vb_load);
+    const int j1 = J(t + 1);
+    if (t + 2 < ntiles && J(t + 2) < Nk) loader.load_k(Kb, J(t + 2), Nk, kb_load);
+    if (j1 < Nk) loader.load_v(Vb, j1, Nk, vb_load);
     u32x4 pb[2][2];
-    if (CAUSAL && kl.partial(t * G::BN, G::BN))  // a diagonal tile (others are full)
-      l += softmax16<E, true>(cur, m, c2, pb, t * G::BN, kl.lane_lim);
+    if (CAUSAL && kl.partial(J(t), G::BN))  // a diagonal tile (others are full)
+      l += softmax16<E, true>(cur, m, c2, pb, J(t), kl.lane_lim);
     else
       l += softmax16<E, false>(cur, m, c2, pb, 0, 0);
     qk16<E, D>(kb_next, qf, nxt);
@@ -385,7 +400,10 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   };
   auto last = [&](int t, const f32x16 (&cur)[2], const lds_u8* vb_cur) {
     u32x4 pb[2][2];
-    const int j0 = t * G::BN;
+    const int j0 = J(t);
+    // a key-split half's tile past the keys: its buffers were never loaded
+    // (a zero P times unloaded LDS could still make NaN), so nothing to add
+    if (KS2 == 2 && j0 >= Nk) return;
     if (kl.partial(j0, G::BN))
       l += softmax16<E, true>(cur, m, c2, pb, j0, kl.lane_lim);
     else
@@ -404,6 +422,36 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     last(t + 1, sB, vbuf1);
   } else {
     last(t, sA, vbuf0);
+  }
+
+  if (KS2 == 2) {
+    // Merge the two halves' states through LDS (the K/V buffers are free once
+    // every wave is past its last PV product).  Half 1 writes its m, l and
+    // acc per lane; half 0 combines.  A half whose row saw no key has l = 0
+    // over the row and contributes nothing (its m may be -inf or NaN).
+    constexpr int NV = G::DB * 16 + 2;  // floats per lane
+    float* const xs = reinterpret_cast<float*>(smem) + (size_t)(rw * 64 + lane) * NV;
+    block_barrier();
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[db * 16 + r] = acc[db][r];
+      xs[G::DB * 16] = m;
+      xs[G::DB * 16 + 1] = l;
+    }
+    block_barrier();
+    if (kh == 1) return;
+    const float m1 = xs[G::DB * 16], l1 = xs[G::DB * 16 + 1];
+    const bool has1 = xhalf_sum(l1) > 0.f;
+    const float mn = has1 ? fmaxf(m, m1) : m;
+    const float a0 = fast_exp2(m - mn), a1 = has1 ? fast_exp2(m1 - mn) : 0.f;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * a0 + (has1 ? xs[db * 16 + r] * a1 : 0.f);
+    l = l * a0 + (has1 ? l1 * a1 : 0.f);
+    m = mn;
   }
 
   // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.
@@ -1106,8 +1154,21 @@ constexpr int kNumCUs = 256;  // MI355X
 bool use_pingpong(int64_t blocks256, int64_t d) {
   const char* env = getenv("ATTN_FWD_KERNEL");
   if (env != nullptr && strcmp(env, "pingpong") == 0) return true;
-  if (env != nullptr && strcmp(env, "pipelined") == 0) return false;
+  if (env != nullptr && (strcmp(env, "pipelined") == 0 || strcmp(env, "pipelined2") == 0))
+    return false;
   return d == 128 && blocks256 >= kNumCUs;
+}
+
+// The pipelined kernel's in-block key split: when the grid of 128-row blocks
+// gives at most one block per CU (one wave per SIMD), without a causal mask
+// or a split and with at least two key tiles.  ATTN_FWD_KERNEL=pipelined
+// turns it off, =pipelined2 forces it where it applies (tests and sweeps).
+bool use_key_split(int64_t blocks128, int64_t N, bool causal, int splits) {
+  if (causal || splits != 1 || N <= 64) return false;
+  const char* env = getenv("ATTN_FWD_KERNEL");
+  if (env != nullptr && strcmp(env, "pipelined2") == 0) return true;
+  if (env != nullptr && strcmp(env, "pipelined") == 0) return false;
+  return blocks128 <= kNumCUs;
 }
 
 template <class E, class T, bool C>
@@ -1118,7 +1179,11 @@ int launch16(const Launch& a) {
     return launch<T>(kern, a.bh * nqt, kPPThreads, (int)nqt, a);
   }
   const int64_t nqt = (a.N + 127) / 128;
-  auto kern = a.d == 128 ? attn_fwd_mfma16<E, 128, C> : attn_fwd_mfma16<E, 64, C>;
+  if (use_key_split(a.bh * nqt, a.N, C, a.splits)) {
+    auto kern = a.d == 128 ? attn_fwd_mfma16<E, 128, false, 2> : attn_fwd_mfma16<E, 64, false, 2>;
+    return launch<T>(kern, a.bh * nqt, 2 * kThreads, (int)nqt, a);
+  }
+  auto kern = a.d == 128 ? attn_fwd_mfma16<E, 128, C, 1> : attn_fwd_mfma16<E, 64, C, 1>;
   return launch<T>(kern, a.bh * nqt, kThreads, (int)nqt, a);
 }
 

@@ -227,10 +227,12 @@ def test_binding_rejects_bad_arguments():
 
 
 # ---------------------------------------------------------------------------
-# both 16-bit kernels (8-wave ping-pong and 4-wave pipelined), forced
+# the 16-bit kernels, forced: 8-wave ping-pong, 4-wave pipelined, and the
+# pipelined kernel with its in-block key split (8 waves; it applies without a
+# causal mask or a split and for N > 64, and falls back to 4 waves otherwise)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined", "pipelined2"])
 @pytest.mark.parametrize("dtype,d,N,BH", [("bf16", 128, 1000, (1, 3)), ("f16", 64, 777, (2, 2)),
                                           ("bf16", 64, 64, (1, 2)), ("f16", 128, 129, (1, 1)),
                                           ("bf16", 128, 1, (2, 1)), ("bf16", 64, 4096, (1, 2)),
@@ -243,14 +245,14 @@ def test_forced_kernel(kernel, dtype, d, N, BH, monkeypatch):
     full_parity(q, k, v, 1.0 / math.sqrt(d), dtype, f"{kernel} {dtype} d={d} N={N}")
 
 
-@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined", "pipelined2"])
 def test_forced_kernel_hot_keys(kernel, monkeypatch):
     monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
     q, k, v = datagen.make_qkv(1, 2, 3000, 128, "bf16", seed=56, hot_frac=0.01, hot_mult=8.0)
     full_parity(q, k, v, 1.0 / math.sqrt(128), "bf16", f"{kernel} hot keys")
 
 
-@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined", "pipelined2"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("direction", [1, -1])
 def test_forced_kernel_moving_max(kernel, d, direction, monkeypatch):
@@ -269,7 +271,7 @@ def test_forced_kernel_moving_max(kernel, d, direction, monkeypatch):
     full_parity(q, k, v, 1.0 / math.sqrt(d), "bf16", f"{kernel} d={d} moving max {direction}")
 
 
-@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined", "pipelined2"])
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 1.5])
 def test_forced_kernel_scales(kernel, scale, monkeypatch):
     """Negative, zero and large scales on each 16-bit kernel."""

@@ -51,7 +51,7 @@ def test_splitkv_shapes(dtype, d, N, splits):
                    f"splitkv {dtype} d={d} N={N} splits={splits}")
 
 
-@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined", "pipelined2"])
 def test_splitkv_both_kernels_hot_keys(kernel, monkeypatch):
     monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
     q, k, v = datagen.make_qkv(1, 2, 3000, 128, "bf16", seed=61, hot_frac=0.01, hot_mult=8.0)

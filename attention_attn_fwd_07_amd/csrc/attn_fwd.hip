@@ -212,8 +212,9 @@ __device__ __forceinline__ void maybe_rescale(float m_tile, float& m, float& l,
 }
 
 // Sum test, the cheaper alternative to the max test (used by the ping-pong
-// kernel without a causal mask): P is first formed against the current reference m, without the
-// tile's row max.  If every lane's sum of its 32 probabilities is at most
+// kernel on every tile that needs no mask): P is first formed against the
+// current reference m, without the tile's row max.  If every lane's sum of
+// its 32 probabilities is at most
 // 2^8, every P is at most 2^8 - the max test's bound - and the tile is done.
 // Otherwise the row max is taken, the rows are rescaled and P is formed
 // again.  The rare path runs whenever the max test would (and also for some
@@ -755,14 +756,9 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // VALU phase of tile t.
   // The rare path forms S again from K_t, which stays in its ring slot until
   // both groups have finished the VALU phase of tile t.
-  // The causal kernel keeps the max test: its extra masking code leaves no
-  // registers for the sum test's second pass.
+  // Full tiles take the sum test; the causal kernel's diagonal tiles keep the
+  // max test (its masking code leaves no registers for the second pass).
   auto valu_full = [&](int t) __attribute__((always_inline)) {
-    if (CAUSAL) {
-      maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
-      l += softmax16<E, false>(sc, m, c2, pb, 0, 0);
-      return;
-    }
     float ps = softmax16<E, false>(sc, m, c2, pb, 0, 0);
     if (__builtin_amdgcn_ballot_w64(ps > kSumLimit) != 0) {  // rare; wave-uniform
       qk_tile<E, D>(lsm, (uint32_t)(t % kRing) * TB, ln, qf, sc);

@@ -11,13 +11,14 @@
 // recomputes its tiles of s and P from Q, K and the stored lse.
 //
 // Three kernels:
-//   * delta:  D = rowsum(dO * O) per query row, into the workspace;
-//   * dq:     one block = 128 query rows; it loops over key tiles and
-//             accumulates dQ^T = K^T dS^T in registers (the forward's layout:
-//             lane l owns query row l % 32 of its wave);
-//   * dkdv:   one block = 128 keys; it loops over query tiles and accumulates
-//             dK^T = Q^T dS and dV^T = dO^T P (the transposed layout: lane l
-//             owns key l % 32 of its wave).
+//   * delta:  per query row the pair (lse log2 e, D = rowsum(dO * O)), into
+//             the workspace;
+//   * dq:     one block = 128 query rows (4 waves); it loops over key tiles
+//             and accumulates dQ^T = K^T dS^T in registers (the forward's
+//             layout: lane l owns query row l % 32 of its wave);
+//   * dkdv:   one block = 256 keys (8 waves); it loops over query tiles and
+//             accumulates dK^T = Q^T dS and dV^T = dO^T P (the transposed
+//             layout: lane l owns key l % 32 of its wave).
 // Each gradient row is owned by exactly one lane pair, so there are no
 // atomics and the results are deterministic.
 //
@@ -528,11 +529,11 @@ int launch_bwd(const attn_bwd_args_t& a, float2* stats, int64_t bh) {
 }
 
 template <class E>
-int launch_bwd_e(const attn_bwd_args_t& a, float2* delta, int64_t bh) {
+int launch_bwd_e(const attn_bwd_args_t& a, float2* stats, int64_t bh) {
   const bool c = (a.flags & ATTN_CAUSAL) != 0;
-  if (a.d == 128) return c ? launch_bwd<E, 128, true>(a, delta, bh)
-                           : launch_bwd<E, 128, false>(a, delta, bh);
-  return c ? launch_bwd<E, 64, true>(a, delta, bh) : launch_bwd<E, 64, false>(a, delta, bh);
+  if (a.d == 128) return c ? launch_bwd<E, 128, true>(a, stats, bh)
+                           : launch_bwd<E, 128, false>(a, stats, bh);
+  return c ? launch_bwd<E, 64, true>(a, stats, bh) : launch_bwd<E, 64, false>(a, stats, bh);
 }
 
 }  // namespace
@@ -579,7 +580,7 @@ extern "C" int attn_bwd(const attn_bwd_args_t* args, void* ws, size_t ws_bytes) 
     if (overlap_b(ws, wb, ptrs[j], sizes[j])) return ATTN_ERR_ALIAS;
 
   // --- launch -------------------------------------------------------------
-  float2* delta = static_cast<float2*>(ws);
-  if (a.dtype == ATTN_DTYPE_BF16) return launch_bwd_e<Bf16T>(a, delta, bh);
-  return launch_bwd_e<F16T>(a, delta, bh);
+  float2* stats = static_cast<float2*>(ws);
+  if (a.dtype == ATTN_DTYPE_BF16) return launch_bwd_e<Bf16T>(a, stats, bh);
+  return launch_bwd_e<F16T>(a, stats, bh);
 }

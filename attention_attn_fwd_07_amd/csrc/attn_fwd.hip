@@ -8,9 +8,18 @@
 // seven steps.  The pages' kernels are Triton programs for NVIDIA parts; this
 // file is a gfx950 design of the same computation.
 //
-// Work unit: one block = 4 wave64s = 128 query rows of one (b, h); each wave
-// owns 32 query rows for the whole key loop.  Key/value tiles of 64 rows are
-// double-buffered through LDS.
+// Kernels (each wave owns 32 query rows of one (b, h) for the whole key loop;
+// K/V tiles of 64 keys stream through LDS by direct global->LDS loads):
+//   * attn_fwd_pp16   bf16/fp16, d = 128, grids of at least one block per CU:
+//                     8 waves, 256 rows, two wave groups taking turns between
+//                     an MFMA phase and a softmax phase (ping-pong);
+//   * attn_fwd_mfma16 bf16/fp16, d = 64 and small grids: 4 waves, 128 rows,
+//                     software-pipelined in each wave; for grids of at most
+//                     one block per CU, 8 waves with the keys split between
+//                     two waves per row group;
+//   * attn_fwd_mfma32 fp32: the same structure on the fp32 MFMA;
+//   * attn_merge      the split-KV merge.
+// All take a causal flag, element strides and a key-range split.
 //
 // Register layouts (the core of the design).  With the 32x32xK MFMA, the C/D
 // fragment of lane l holds column (l % 32) and rows 8*(r/4) + 4*(l/32) + r%4

@@ -13,7 +13,9 @@
  * computed tile by tile with an online softmax (page 1 "Triton hand-written
  * kernels", section 4: running row max m, running exp-sum l, rescaled fp32
  * accumulator), so the N x N score matrix never reaches device memory.
- * Self-attention (queries and keys share N), non-causal.
+ * Self-attention (queries and keys share N).  attn_fwd is the non-causal
+ * call on contiguous tensors; attn_fwd_ex adds the causal variant and element
+ * strides, attn_fwd_splitkv splits each head's keys over several blocks.
  *
  * Everything here is plain C: pointers, sizes and an opaque stream handle.
  */

@@ -122,7 +122,7 @@ def padded(t, pad):
     return buf[..., :d]
 
 
-@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined", "pipelined2"])
 @pytest.mark.parametrize("dtype,d,N", [("bf16", 128, 1000), ("f16", 64, 513), ("bf16", 64, 64),
                                        ("f32", 64, 300), ("f32", 128, 77)])
 @pytest.mark.parametrize("causal", [False, True])

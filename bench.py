@@ -15,7 +15,10 @@ torch's current stream, bracketed by torch.cuda.synchronize() on both sides
 (wall clock for ms_per_step) and by two HIP events recorded on that same
 stream just before the first and just after the last launch (mean kernel
 duration for the roofline).  The launches go through a plan that marshals the
-arguments once, so the host keeps ahead of the GPU.
+arguments once, so the host keeps ahead of the GPU.  After the timed region,
+single launches are timed one by one for p20 / median / p80 (kernel_ms), and
+for the two small workloads also after a 512 MB write that evicts L2 and the
+Infinity Cache (kernel_ms.cold).
 
 Roofline: flops = 4*B*H*N^2*d per launch against the dense bf16/fp16 MFMA
 peak of 2500 TFLOP/s (fp32 workloads: 157.3 TFLOP/s fp32 matrix peak).
@@ -114,6 +117,29 @@ def cpu_baseline(w, q, k, v, budget_s: float = 10.0):
             "sample": f"{done} of {total} query rows (units of {rows_per_unit} rows of one head),"
                       f" each against all {w.N} keys; fp64 numpy on {cores} threads; {dt:.1f} s",
             "full_workload_seconds_extrapolated": round(dt * total / done, 1)}
+
+
+def per_launch_ms(launch, stream, reps: int, flush=None) -> dict:
+    """Kernel time of single launches (HIP events on the launch stream around
+    each one), as p20 / median / p80 in ms.  With ``flush``, it runs before
+    every launch (outside the events) to evict L2 and the Infinity Cache."""
+    import torch
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+
+    def pct(p):
+        return round(times[min(len(times) - 1, int(p * len(times)))], 5)
+    return {"p20": pct(0.2), "median": pct(0.5), "p80": pct(0.8), "n": len(times)}
 
 
 def calibrate_copy(nbytes: int, reps: int) -> None:
@@ -222,6 +248,16 @@ def main(argv=None) -> int:
 
     kern_ms = ev0.elapsed_time(ev1) / K  # HIP events on the launch stream, K launches
     ms_per_step = wall * 1e3 / K
+
+    # After the timed region: the per-launch spread, and for the small
+    # workloads the same with L2 and the 256 MB Infinity Cache flushed first
+    # by writing a 512 MB buffer (cold inputs).
+    dist = per_launch_ms(launch, stream, max(10, min(K, 50)))
+    cold = None
+    if w.key in (1, 2):
+        flushbuf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = per_launch_ms(launch, stream, 20, flush=lambda: flushbuf.fill_(1))
+        del flushbuf
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -242,7 +278,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": dict(w.describe(), mode=mode, causal=bool(args.causal)),
         "pct_of_peak": round(100.0 * value / peak, 2),
-        "kernel_ms": {"mean": round(kern_ms, 5)},
+        "kernel_ms": dict({"mean": round(kern_ms, 5)}, **{k: v for k, v in dist.items()},
+                          **({"cold": cold} if cold else {})),
         "hbm_gbps_algorithmic": (round(algorithmic_bytes(w) / (kern_ms * 1e-3) / 1e9, 1)
                                  if not args.backward else None),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,

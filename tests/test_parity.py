@@ -113,6 +113,26 @@ def test_workload_sampled_parity(key):
     assert np.all(o >= lo) and np.all(o <= hi)
 
 
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 64, 1 << 20), ("f16", 128, (1 << 19) + 37)])
+def test_long_sequence_sampled(dtype, d, N):
+    """One head of 2^20 keys (d = 64) and of 2^19 + 37 (d = 128, ragged): the
+    largest sequences here, far past the workloads' lengths (byte offsets of
+    a head up to 2^28, 2^14 key tiles per block), on sampled rows the oracle
+    computes exactly plus the convex-hull property on every row."""
+    q, k, v = datagen.make_qkv(1, 1, N, d, dtype, seed=N % 1000)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_gpu(q, k, v, scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    idx = _sample_index(o, 1, 1, N, np.random.default_rng(N % 997), per_head=40, top=24)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, idx)
+    b, h, i = idx[:, 0], idx[:, 1], idx[:, 2]
+    check(o[b, h, i], lse[b, h, i], o_ref, lse_ref, dtype, f"N={N} d={d} ({len(idx)} rows)")
+    v64 = v.double().numpy()
+    lo = v64.min(axis=2, keepdims=True) - TOL[dtype]["maxabs"]
+    hi = v64.max(axis=2, keepdims=True) + TOL[dtype]["maxabs"]
+    assert np.all(o >= lo) and np.all(o <= hi)
+
+
 # ---------------------------------------------------------------------------
 # ragged and small shapes, every dtype and head dim
 # ---------------------------------------------------------------------------

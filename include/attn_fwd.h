@@ -82,6 +82,8 @@ enum {
  * stream  : a hipStream_t (NULL = the null stream).  The launch is
  *           asynchronous and ordered on this stream; the call never
  *           synchronises, allocates or frees anything, and keeps no state.
+ *           It enqueues kernel launches only (no memset or copy), so it may
+ *           be captured into a HIP graph and replayed.
  *
  * Ownership: the caller owns every buffer and must keep them alive until the
  * stream work completes.  Pointers must be device memory of the current

@@ -276,7 +276,6 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const float2 st = qrow < N ? stats[(size_t)bh * N + qrow] : make_float2(INFINITY, 0.f);
   const float lse2 = st.x, dl = st.y;
   const int lim = CAUSAL ? min(N - 1, qrow) : N - 1;         // last key this row sees
-  const int wlim = CAUSAL ? min(N - 1, q0 + wave * 32) : N - 1;  // smallest over the wave
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
@@ -289,46 +288,125 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __asm__ volatile("" ::"v"(lse2), "v"(dl));
   __syncthreads();
 
-  const FragOff<D> fo;
-  for (int t = 0; t < T; ++t) {
+  FragOff<D> fo;
+  // A operand of MFMA i of the S / dP products of half sb: even i the K row
+  // fragment of k-step i / 2 (into S), odd i the V row fragment (into dP).
+  auto sdp_a = [&](const Tile<D>& kt, const Tile<D>& vt, int sb, int i)
+      __attribute__((always_inline)) -> u32x4 {
+    return (i & 1) ? vt.row_op(fo, 32 * sb, i >> 1) : kt.row_op(fo, 32 * sb, i >> 1);
+  };
+  // One element r of dS = P (dP - D), from S and dP.  In a masked tile, key
+  // 32 sb + 8 (r / 4) + 4 hh + r % 4 of the tile is visible to the lane's row
+  // if 32 sb + 8 (r / 4) + r % 4 <= xlim = lim - j0 - 4 hh (one compare with
+  // a constant).
+  // The value passes through an empty asm statement, which pins its
+  // computation to the step that asks for it (the compiler would otherwise
+  // sink it to the packing that consumes it).
+  auto ds_elem = [&](int xlim, int sb, int r, bool masked, float sv, float dpv)
+      __attribute__((always_inline)) -> float {
+    float p = fast_exp2(fmaf(sv, c2, -lse2));
+    if (masked && 32 * sb + 8 * (r >> 2) + (r & 3) > xlim) p = 0.f;
+    float x = p * (dpv - dl);
+    __asm__ volatile("" : "+v"(x));
+    return x;
+  };
+  // One tile.  Its two 32-key halves are staggered so that the softmax
+  // arithmetic of one half issues between the MFMAs of the other half's
+  // products, in this order (each step a straight run of instructions):
+  //   1. S0 = K0 Q^T, dP0 = V0 dO^T                       16 MFMAs (d = 128)
+  //   2. S1, dP1, and element i of dS0 after MFMA i        16 MFMAs + dS0
+  //   3. dQ^T += K0^T dS0^T, elements 2i, 2i+1 of dS1     8 MFMAs + dS1
+  //   4. dQ^T += K1^T dS1^T                                8 MFMAs
+  // masked: some keys of the tile lie past a row's limit (tail or diagonal).
+  constexpr int NS = 2 * KS;  // MFMAs of S and dP per half
+  // Step 1 (needs no mask).
+  auto step1 = [&](const Tile<D>& kt, const Tile<D>& vt, f32x16& s0, f32x16& dp0)
+      __attribute__((always_inline)) {
+    s0 = (f32x16){};
+    dp0 = (f32x16){};
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i & 1)
+        dp0 = E::mfma(sdp_a(kt, vt, 0, i), df[i >> 1], dp0);
+      else
+        s0 = E::mfma(sdp_a(kt, vt, 0, i), qf[i >> 1], s0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Steps 2-4.
+  auto steps234 = [&](const Tile<D>& kt, const Tile<D>& vt, int j0, bool masked, f32x16& s0,
+                      const f32x16& dp0) __attribute__((always_inline)) {
+    f32x16 s1 = (f32x16){}, dp1 = (f32x16){};
+    int xlim = lim - j0 - 4 * hh;
+    __asm__ volatile("" : "+v"(xlim));  // kept whole: no per-element offsets hoisted
+    // 2.  The operand of MFMA i + 2 is read before MFMA i issues; dS
+    // replaces S in place.
+    u32x4 a[NS];
+    a[0] = sdp_a(kt, vt, 1, 0);
+    a[1] = sdp_a(kt, vt, 1, 1);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + 2 < NS) a[i + 2] = sdp_a(kt, vt, 1, i + 2);
+      if (i & 1)
+        dp1 = E::mfma(a[i], df[i >> 1], dp1);
+      else
+        s1 = E::mfma(a[i], qf[i >> 1], s1);
+#pragma unroll
+      for (int r = i * 16 / NS; r < (i + 1) * 16 / NS; ++r)
+        s0[r] = ds_elem(xlim, 0, r, masked, s0[r], dp0[r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    u32x4 pb0[2], pb1[2];
+    pack_frag<E>(s0, pb0);
+    __builtin_amdgcn_sched_barrier(0);
+    // 3.
+    constexpr int NQ = 2 * DB;  // MFMAs of dQ per half
+    u32x4 b[NQ];
+    b[0] = kt.tr_op(fo, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int db = i >> 1, hq = i & 1;
+      if (i + 1 < NQ) b[i + 1] = kt.tr_op(fo, 16 * ((i + 1) & 1), (i + 1) >> 1);
+      acc[db] = E::mfma(b[i], pb0[hq], acc[db]);
+#pragma unroll
+      for (int r = i * 16 / NQ; r < (i + 1) * 16 / NQ; ++r)
+        s1[r] = ds_elem(xlim, 1, r, masked, s1[r], dp1[r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pack_frag<E>(s1, pb1);
+    __builtin_amdgcn_sched_barrier(0);
+    // 4.
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq)
+        acc[db] = E::mfma(kt.tr_op(fo, 32 + 16 * hq, db), pb1[hq], acc[db]);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto run_tile = [&](int t, bool masked) __attribute__((always_inline)) {
     const int buf = t & 1;
     if (t + 1 < T) load(t + 1, buf ^ 1);
     const Tile<D> kt{lsm + (2 * buf) * TB}, vt{lsm + (2 * buf + 1) * TB};
-    const int j0 = t * kBN;
-    const bool partial = j0 + kBN - 1 > wlim;
-    // one 32-key half of the tile at a time (fewer live registers)
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      f32x16 s = (f32x16){}, dp = (f32x16){};
-      // MFMA sections run at raised priority, so that the SIMD's other wave,
-      // when it is in its exponential section, fills the issue gaps instead.
-      __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = E::mfma(kt.row_op(fo, 32 * sb, ks), qf[ks], s);
-        dp = E::mfma(vt.row_op(fo, 32 * sb, ks), df[ks], dp);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      f32x16 ds;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], c2, -lse2));
-        if (partial && j0 + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3) > lim) p = 0.f;
-        ds[r] = p * (dp[r] - dl);
-      }
-      u32x4 pb[2];
-      pack_frag<E>(ds, pb);
-      __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int hq = 0; hq < 2; ++hq)
-          acc[db] = E::mfma(kt.tr_op(fo, 32 * sb + 16 * hq, db), pb[hq], acc[db]);
-      __builtin_amdgcn_s_setprio(0);
-    }
+    // Fresh copies of the lane offsets each tile, so that the per-fragment
+    // XORs are formed where they are used instead of being hoisted out of
+    // the loop into a register each.
+    __asm__ volatile("" : "+v"(fo.row), "+v"(fo.tra), "+v"(fo.trb));
+    f32x16 s0, dp0;
+    step1(kt, vt, s0, dp0);
+    steps234(kt, vt, t * kBN, masked, s0, dp0);
     wait_vmcnt<0>();
     __syncthreads();
-  }
+  };
+  // Tiles below TF are visible in full to every row of the block; the rest
+  // (the sequence tail, the causal diagonal) take the mask.
+  const int TF = min(T, ((CAUSAL ? min(N - 1, q0) : N - 1) + 1) / kBN);
+  int t = 0;
+  for (; t < TF; ++t) run_tile(t, false);
+  for (; t < T; ++t) run_tile(t, true);
   if (qrow < N) store_grad_row<E, D>(dQ + hoff, qrow, acc, scale);
 }
 

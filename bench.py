@@ -28,14 +28,25 @@ the kernel source is unchanged since those counters were taken.
 
 cpu_baseline: the fp64 CPU oracle, as it stands, timed on this host's cores on
 a bounded sample of the same workload (whole heads until ~10 s have passed).
+
+clock: while the timed launches run, a thread samples the shader clock the
+driver reports (the current level of sysfs pp_dpm_sclk) and the socket power
+(hwmon power1_input); ``frac_at_clock`` relates the achieved rate to the peak
+at that clock (the spec peaks are quoted at 2.4 GHz).  From an idle GPU the
+throughput takes some 25 ms of back-to-back launches to settle, hence the
+defaults: at least 0.3 s of warmup launches, then about 1 s of timed ones
+(both at least 200; --warmup and --steps set exact counts).
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
+import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -142,6 +153,117 @@ def per_launch_ms(launch, stream, reps: int, flush=None) -> dict:
     return {"p20": pct(0.2), "median": pct(0.5), "p80": pct(0.8), "n": len(times)}
 
 
+SPEC_CLOCK_MHZ = 2400.0
+
+
+def gpu_sysfs_dir():
+    """The GPU's sysfs device directory: the one card that reports shader clock
+    levels (None if there is none, or several, which could not be told apart)."""
+    cards = [d for d in sorted(glob.glob("/sys/class/drm/card*/device"))
+             if os.path.exists(os.path.join(d, "pp_dpm_sclk"))]
+    return cards[0] if len(cards) == 1 else None
+
+
+def parse_sclk(text: str):
+    """Current shader clock in MHz from pp_dpm_sclk (the starred line)."""
+    m = re.search(r"(\d+)\s*Mhz\s*\*", text, re.IGNORECASE)
+    return float(m.group(1)) if m else None
+
+
+class ClockSampler:
+    """Samples the shader clock and the socket power from sysfs on a thread,
+    every ``period_s`` seconds between __enter__ and __exit__."""
+
+    def __init__(self, period_s: float = 0.002, sysfs_dir=None):
+        self.dir = sysfs_dir if sysfs_dir is not None else gpu_sysfs_dir()
+        self.period = period_s
+        self.sclk, self.power = [], []
+        self.window_s = 0.0
+        self._stop = threading.Event()
+        self._thread = None
+        hw = sorted(glob.glob(os.path.join(self.dir, "hwmon", "hwmon*"))) if self.dir else []
+        self._hwmon = hw[0] if hw else None
+
+    def _read(self, path):
+        try:
+            with open(path) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            t = self._read(os.path.join(self.dir, "pp_dpm_sclk"))
+            f = parse_sclk(t) if t else None
+            if f is not None:
+                self.sclk.append(f)
+            if self._hwmon:
+                pw = self._read(os.path.join(self._hwmon, "power1_input"))
+                if pw and pw.strip().isdigit():
+                    self.power.append(int(pw) * 1e-6)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._t0 = time.perf_counter()
+        if self.dir:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+        self.window_s = time.perf_counter() - self._t0
+        return False
+
+    def summary(self, achieved: float, peak: float):
+        """Mean clock and power over the samples, and the achieved rate as a
+        fraction of the peak at the mean clock; None without samples.  The
+        driver's figures are averages over its own window (some tenths of a
+        second), so over a shorter run they still carry the idle clock:
+        frac_at_clock is given only for windows of at least 0.25 s."""
+        if not self.sclk:
+            return None
+        f = sum(self.sclk) / len(self.sclk)
+        cap = self._read(os.path.join(self._hwmon, "power1_cap")) if self._hwmon else None
+        peak_f = peak * f / SPEC_CLOCK_MHZ
+        long_enough = self.window_s >= 0.25
+        return {"sclk_mhz": round(f, 1), "sclk_mhz_min": min(self.sclk),
+                "sclk_mhz_max": max(self.sclk), "samples": len(self.sclk),
+                "window_s": round(self.window_s, 3),
+                "power_w": round(sum(self.power) / len(self.power), 1) if self.power else None,
+                "power_cap_w": (round(int(cap) * 1e-6, 1) if cap and cap.strip().isdigit()
+                                else None),
+                "peak_at_clock": round(peak_f, 1) if long_enough else None,
+                "frac_at_clock": round(achieved / peak_f, 4) if long_enough else None,
+                "source": "sysfs pp_dpm_sclk (current level), hwmon power1_input"}
+
+
+def time_batch(launch, n: int) -> float:
+    """Seconds for n back-to-back launches (synchronised on both sides)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        launch()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def auto_warmup(launch, min_launches: int, min_seconds: float):
+    """Untimed launches in batches of 20 until at least ``min_launches`` and
+    ``min_seconds`` have passed (the shader clock ramps up from idle over the
+    first tens of milliseconds of load).  Returns (launches, seconds per
+    launch in the last batch)."""
+    n, t, last = 0, 0.0, 0.0
+    while n < min_launches or t < min_seconds:
+        last = time_batch(launch, 20)
+        n += 20
+        t += last
+    return n, last / 20
+
+
 def calibrate_copy(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -157,8 +279,10 @@ def calibrate_copy(nbytes: int, reps: int) -> None:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed launches (default: enough for about 1 s, at least 200)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed launches first (default: about 0.3 s of them, at least 200)")
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
@@ -174,6 +298,9 @@ def main(argv=None) -> int:
                          "flops counted as 10 B H N^2 d (the five products; N(N+1)/2 pairs "
                          "in place of N^2 when causal)")
     args = ap.parse_args(argv)
+    if (args.steps is not None and args.steps < 1) or (args.warmup is not None and args.warmup < 0):
+        print("bench.py: --steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+        return 2
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this attention forward runs on one GPU; multi-GPU runs are not "
@@ -184,7 +311,7 @@ def main(argv=None) -> int:
     import torch
 
     if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        calibrate_copy(args.calibrate_copy, max(1, args.steps or 3))
         return 0
 
     import attention_attn_fwd_07_amd as attn
@@ -232,19 +359,27 @@ def main(argv=None) -> int:
         launch = attn.plan(qd, kd, vd, o, lse, w.scale, stream, causal=args.causal)
     if args.causal:
         mode += " causal"
-    for _ in range(args.warmup):
-        launch()
-    K = args.steps
+    if args.warmup is not None:
+        W = args.warmup
+        t_w = time_batch(launch, W) if W > 0 else 0.0
+        per_launch_s = t_w / W if W > 0 else None
+    else:
+        W, per_launch_s = auto_warmup(launch, min_launches=200, min_seconds=0.3)
+    if args.steps is not None:
+        K = args.steps
+    else:
+        K = 200 if per_launch_s is None else max(200, min(100000, int(1.0 / per_launch_s)))
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(K):
-        launch()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(K):
+            launch()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     kern_ms = ev0.elapsed_time(ev1) / K  # HIP events on the launch stream, K launches
     ms_per_step = wall * 1e3 / K
@@ -269,7 +404,7 @@ def main(argv=None) -> int:
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": W,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -285,6 +420,7 @@ def main(argv=None) -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_for(w) if mode == "fwd" else None},
+        "clock": clock.summary(achieved, peak),
         "kernel_sha256_16": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

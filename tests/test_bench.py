@@ -1,6 +1,7 @@
 """bench.py: host logic on the CPU, and the one-line JSON contract on the GPU."""
 import json
 import math
+import time
 
 import pytest
 
@@ -70,5 +71,52 @@ def test_bench_json_line(extra, capsys):
     assert 0.0 < r["achieved"] < r["peak"]
     assert math.isclose(r["frac"], r["achieved"] / r["peak"], rel_tol=1e-3, abs_tol=1e-4)
     assert d["value"] > 0 and d["ms_per_step"] > 0
+    c = d["clock"]  # None where the driver's sysfs files are not readable
+    if c is not None:
+        assert c["samples"] >= 1 and 0 < c["sclk_mhz"] <= 3000
+        if c["frac_at_clock"] is not None:
+            assert math.isclose(c["frac_at_clock"], r["achieved"] / c["peak_at_clock"],
+                                rel_tol=1e-2)
     if "--backward" in extra:
         assert d["metric"].startswith("attention bwd")
+
+
+def test_parse_sclk_reads_the_current_level():
+    assert bench.parse_sclk("0: 500Mhz\n1: 1650Mhz *\n2: 2400Mhz\n") == 1650.0
+    assert bench.parse_sclk("S: 94Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 94.0
+    assert bench.parse_sclk("0: 500Mhz\n1: 2400Mhz\n") is None
+
+
+def test_clock_sampler_summary(tmp_path):
+    (tmp_path / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 1600Mhz *\n2: 2400Mhz\n")
+    hw = tmp_path / "hwmon" / "hwmon0"
+    hw.mkdir(parents=True)
+    (hw / "power1_input").write_text("1290000000\n")
+    (hw / "power1_cap").write_text("1400000000\n")
+    with bench.ClockSampler(period_s=0.005, sysfs_dir=str(tmp_path)) as c:
+        time.sleep(0.3)
+    s = c.summary(achieved=1200.0, peak=2500.0)
+    assert s["samples"] >= 2 and s["sclk_mhz"] == 1600.0 and s["window_s"] >= 0.25
+    assert s["power_w"] == 1290.0 and s["power_cap_w"] == 1400.0
+    assert math.isclose(s["peak_at_clock"], 2500.0 * 1600 / 2400, rel_tol=1e-3)
+    assert math.isclose(s["frac_at_clock"], 1200.0 / (2500.0 * 1600 / 2400), rel_tol=1e-3)
+
+
+def test_clock_sampler_without_sysfs_reports_nothing(tmp_path):
+    with bench.ClockSampler(period_s=0.001, sysfs_dir=str(tmp_path)) as c:
+        time.sleep(0.01)
+    assert c.summary(1.0, 2.0) is None
+
+
+def test_short_window_gives_no_clock_fraction(tmp_path):
+    (tmp_path / "pp_dpm_sclk").write_text("1: 1100Mhz *\n")
+    with bench.ClockSampler(period_s=0.001, sysfs_dir=str(tmp_path)) as c:
+        time.sleep(0.02)
+    s = c.summary(achieved=1200.0, peak=2500.0)
+    assert s["sclk_mhz"] == 1100.0 and s["frac_at_clock"] is None and s["peak_at_clock"] is None
+
+
+def test_step_counts_are_checked(capsys):
+    assert bench.main(["--steps", "0"]) == 2
+    assert bench.main(["--warmup", "-1"]) == 2
+    assert "--steps" in capsys.readouterr().err

@@ -117,6 +117,45 @@ __device__ __forceinline__ void store_row16(uint16_t* __restrict__ Oh, float* __
 }
 
 
+// The final O rows of one wave (32 rows) stored through LDS so that each
+// global store instruction writes whole rows: the C fragments (lane l: row
+// l % 32, columns 32 db + 8 g + 4 (l / 32) .. +3) are normalised, rounded
+// and written to the wave's own LDS area of 32 x 2D bytes as row-major rows
+// whose 16-byte chunks are XOR-swizzled by the row (so the 32 rows of one
+// write instruction spread over the banks), then read back 16 bytes per lane
+// and stored, 64 / (D / 8) whole rows per instruction.  Storing straight from
+// the fragments would write 16-byte pieces of 32 rows per instruction, four
+// times the memory transactions for the same bytes.  lse is written as
+// before (lanes of half 0, consecutive rows).
+template <class E, int D>
+__device__ __forceinline__ void store_rows_lds(lds_u8* area, uint16_t* __restrict__ Oh,
+                                               float* __restrict__ LSE, const Layout& L, int bh,
+                                               int N, int row0, const f32x16 (&acc)[D / 32],
+                                               float inv, float lse) {
+  constexpr int ROWB = 2 * D, CH = D / 8, RPI = 64 / CH;
+  const int lane = threadIdx.x & 63, li = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 4 * db + g;
+      const u32x2 w = (u32x2){E::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                              E::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          area + li * ROWB + ((c ^ (li & (CH - 1))) << 4) + 8 * hh) = w;
+    }
+  // the wave's LDS operations complete in order; this keeps the compiler
+  // from moving the reads above the writes
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CH, c = lane % CH;
+    const u32x4 x = *(const lds_u32x4*)(area + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
+    if (row0 + r < N) *reinterpret_cast<u32x4*>(Oh + (size_t)(row0 + r) * L.o[2] + 8 * c) = x;
+  }
+  if (LSE != nullptr && hh == 0 && row0 + li < N) LSE[(size_t)bh * N + row0 + li] = lse;
+}
+
 // --- pieces of one K/V tile -------------------------------------------------
 
 // S^T = K Q^T for the two 32-key halves of a 64-key tile.  s[sb][r] is the
@@ -859,9 +898,19 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
-  if (qrow < N)
-    store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv,
-                      (m + log2f(lt)) * kLn2);
+  const float lse = (m + log2f(lt)) * kLn2;
+  if (sp.len) {
+    if (qrow < N) store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv, lse);
+  } else {
+    static_assert(kPPThreads / 64 * 32 * 2 * D <= kRing * G::TILEB,
+                  "the output staging must fit in the K ring");
+    // The K ring is free here: its last reader, the VALU phase of the last
+    // tile (whose rare path may form S again from K), ended at this wave's
+    // last barrier, and every tile load has landed.  Wave w takes bytes
+    // w * 32 * 2D .. of it (8 waves x 8 KiB = the 4 K slots at d = 128).
+    store_rows_lds<E, D>((lds_u8*)smem + wave * 32 * 2 * D, Oh, LSE, L, bh, N,
+                         qt * BM + wave * 32, acc, inv, lse);
+  }
 }
 
 // ---------------------------------------------------------------------------

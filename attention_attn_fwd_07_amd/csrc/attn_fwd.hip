@@ -473,12 +473,12 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     last(t, sA, vbuf0);
   }
 
+  constexpr int NV = G::DB * 16 + 2;  // floats per lane in the key-split merge
   if (KS2 == 2) {
     // Merge the two halves' states through LDS (the K/V buffers are free once
     // every wave is past its last PV product).  Half 1 writes its m, l and
     // acc per lane; half 0 combines.  A half whose row saw no key has l = 0
     // over the row and contributes nothing (its m may be -inf or NaN).
-    constexpr int NV = G::DB * 16 + 2;  // floats per lane
     float* const xs = reinterpret_cast<float*>(smem) + (size_t)(rw * 64 + lane) * NV;
     block_barrier();
     if (kh == 1) {
@@ -506,9 +506,19 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.
   const float lt = xhalf_sum(l);
   const float inv = 1.0f / lt;
-  if (qrow < N)
-    store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv,
-                      (m + log2f(lt)) * kLn2);
+  const float lse = (m + log2f(lt)) * kLn2;
+  if (sp.len) {
+    if (qrow < N) store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv, lse);
+  } else {
+    // Output staging: without the key split, the two K buffers (every wave
+    // read its last K tile before the last barrier it passed; only V is still
+    // read); with it, this wave's own part of the merge area, which only
+    // this wave has read since the merge's barrier.
+    static_assert(4 * 32 * 2 * D <= 2 * G::TILEB && 32 * 2 * D <= 64 * NV * 4,
+                  "the output staging must fit");
+    lds_u8* const area = KS2 == 2 ? (lds_u8*)smem + rw * 64 * NV * 4 : kbuf0 + rw * 32 * 2 * D;
+    store_rows_lds<E, D>(area, Oh, LSE, L, bh, N, qt * BM + rw * 32, acc, inv, lse);
+  }
 }
 
 // --- MFMA phase with lean registers ---------------------------------------

@@ -303,8 +303,8 @@ def main(argv=None) -> int:
         return 2
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this attention forward runs on one GPU; multi-GPU runs are not "
-              "part of this build (heads or batches would shard with no communication).",
+        print("bench.py: this attention forward runs on one GPU; several-GPU runs are not "
+              "supported (heads or batches would shard with no communication).",
               file=sys.stderr)
         return 2
 

@@ -113,12 +113,13 @@ def test_workload_sampled_parity(key):
     assert np.all(o >= lo) and np.all(o <= hi)
 
 
-@pytest.mark.parametrize("dtype,d,N", [("bf16", 64, 1 << 20), ("f16", 128, (1 << 19) + 37)])
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 64, 1 << 22), ("f16", 128, (1 << 19) + 37)])
 def test_long_sequence_sampled(dtype, d, N):
-    """One head of 2^20 keys (d = 64) and of 2^19 + 37 (d = 128, ragged): the
-    largest sequences here, far past the workloads' lengths (byte offsets of
-    a head up to 2^28, 2^14 key tiles per block), on sampled rows the oracle
-    computes exactly plus the convex-hull property on every row."""
+    """One head of 2^22 keys (d = 64; the largest N the library accepts,
+    ATTN_MAX_N) and of 2^19 + 37 (d = 128, ragged): far past the workloads'
+    lengths (byte offsets of a head up to 2^29, 2^16 key tiles per block), on
+    sampled rows the oracle computes exactly plus the convex-hull property on
+    every row."""
     q, k, v = datagen.make_qkv(1, 1, N, d, dtype, seed=N % 1000)
     scale = 1.0 / math.sqrt(d)
     o, lse = run_gpu(q, k, v, scale)

@@ -120,3 +120,16 @@ def test_step_counts_are_checked(capsys):
     assert bench.main(["--steps", "0"]) == 2
     assert bench.main(["--warmup", "-1"]) == 2
     assert "--steps" in capsys.readouterr().err
+
+
+@pytest.mark.gpu
+def test_bench_default_counts_are_time_based(capsys):
+    """Without --steps/--warmup: at least 200 warmup launches over >= 0.3 s,
+    then at least 200 timed ones over about a second."""
+    assert bench.main(["--workload", "2", "--no-cpu-baseline"]) == 0
+    d = json.loads([x for x in capsys.readouterr().out.splitlines() if x.strip()][-1])
+    assert d["warmup"] >= 200 and d["steps"] >= 200
+    assert d["steps"] * d["ms_per_step"] >= 500.0  # about 1 s of timed launches
+    c = d["clock"]
+    if c is not None:
+        assert c["window_s"] >= 0.5 and c["frac_at_clock"] is not None

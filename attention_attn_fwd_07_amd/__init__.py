@@ -165,10 +165,31 @@ def _raise_for(rc: int) -> None:
 
 
 def _strides(t):
-    """(batch, head, row) element strides, or zeros for a contiguous tensor."""
+    """(batch, head, row) element strides, or zeros for a contiguous tensor.
+
+    All-zero strides are the C ABI's mark of a contiguous tensor, so a
+    non-contiguous tensor whose three leading strides are all zero (one row
+    broadcast to every (b, h, n), as ``t[:1, :1, :1].expand(...)`` makes) has
+    no stride triple of its own; ``_unbroadcast`` handles it before this."""
     if t.is_contiguous():
         return (0, 0, 0)
-    return tuple(int(x) for x in t.stride()[:3])
+    st = tuple(int(x) for x in t.stride()[:3])
+    if st == (0, 0, 0):
+        raise ValueError("a tensor broadcast from a single row has no stride triple; "
+                         "pass it through _unbroadcast (inputs) or use a real output")
+    return st
+
+
+def _unbroadcast(t, name: str, output: bool = False):
+    """An input whose batch, head and row strides are all zero (one row
+    broadcast over the whole [B, H, N, d] shape) is copied to a contiguous
+    tensor with the same values; an output of that form cannot hold distinct
+    rows and is rejected."""
+    if t.numel() == 0 or t.is_contiguous() or tuple(t.stride()[:3]) != (0, 0, 0):
+        return t
+    if output:
+        raise ValueError(f"{name}: an output broadcast from a single row cannot hold the result")
+    return t.contiguous()
 
 
 class Plan:
@@ -184,6 +205,8 @@ class Plan:
                  splits: int = 0, workspace=None):
         torch = _torch()
         code_dtype = _check(q, k, v, o, lse)
+        q, k, v = (_unbroadcast(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+        _unbroadcast(o, "o", output=True)
         B, H, N, d = (int(x) for x in q.shape)
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream

@@ -1360,7 +1360,10 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
         return ATTN_ERR_LAYOUT;
     }
     // the kernels address a head's rows with 32-bit byte offsets
-    if (N * st[t][2] * (int64_t)esize >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    int64_t head_bytes = 0;
+    if (!mul_ok(N, st[t][2], &head_bytes) || !mul_ok(head_bytes, (int64_t)esize, &head_bytes) ||
+        head_bytes >= ((int64_t)1 << 31))
+      return ATTN_ERR_SHAPE;
   }
   if (!rows_disjoint(st[3], B, H, N, d)) return ATTN_ERR_LAYOUT;
 

@@ -217,27 +217,40 @@ class ClockSampler:
         self.window_s = time.perf_counter() - self._t0
         return False
 
+    # The driver's clock and power figures are averages over its own window of
+    # some tenths of a second: over a shorter run they still describe the idle
+    # GPU before it (a 6 ms run once read 345 MHz while it ran at well over
+    # 1.5 GHz), so below this window nothing measured is reported.
+    MIN_WINDOW_S = 0.25
+
     def summary(self, achieved: float, peak: float):
         """Mean clock and power over the samples, and the achieved rate as a
-        fraction of the peak at the mean clock; None without samples.  The
-        driver's figures are averages over its own window (some tenths of a
-        second), so over a shorter run they still carry the idle clock:
-        frac_at_clock is given only for windows of at least 0.25 s."""
+        fraction of the peak at the mean clock; None without samples.  For a
+        window shorter than MIN_WINDOW_S the clock, power and fraction fields
+        are null (only the window and the sample count are given)."""
         if not self.sclk:
             return None
-        f = sum(self.sclk) / len(self.sclk)
         cap = self._read(os.path.join(self._hwmon, "power1_cap")) if self._hwmon else None
+        out = {"sclk_mhz": None, "sclk_mhz_min": None, "sclk_mhz_max": None,
+               "samples": len(self.sclk), "window_s": round(self.window_s, 3),
+               "power_w": None,
+               "power_cap_w": (round(int(cap) * 1e-6, 1) if cap and cap.strip().isdigit()
+                               else None),
+               "peak_at_clock": None, "frac_at_clock": None,
+               "source": "sysfs pp_dpm_sclk (current level), hwmon power1_input"}
+        if self.window_s < self.MIN_WINDOW_S:
+            out["note"] = (f"window under {self.MIN_WINDOW_S} s: the driver's clock and power "
+                           "averages would describe the idle GPU before the run")
+            return out
+        f = sum(self.sclk) / len(self.sclk)
         peak_f = peak * f / SPEC_CLOCK_MHZ
-        long_enough = self.window_s >= 0.25
-        return {"sclk_mhz": round(f, 1), "sclk_mhz_min": min(self.sclk),
-                "sclk_mhz_max": max(self.sclk), "samples": len(self.sclk),
-                "window_s": round(self.window_s, 3),
-                "power_w": round(sum(self.power) / len(self.power), 1) if self.power else None,
-                "power_cap_w": (round(int(cap) * 1e-6, 1) if cap and cap.strip().isdigit()
+        out.update({"sclk_mhz": round(f, 1), "sclk_mhz_min": min(self.sclk),
+                    "sclk_mhz_max": max(self.sclk),
+                    "power_w": (round(sum(self.power) / len(self.power), 1) if self.power
                                 else None),
-                "peak_at_clock": round(peak_f, 1) if long_enough else None,
-                "frac_at_clock": round(achieved / peak_f, 4) if long_enough else None,
-                "source": "sysfs pp_dpm_sclk (current level), hwmon power1_input"}
+                    "peak_at_clock": round(peak_f, 1),
+                    "frac_at_clock": round(achieved / peak_f, 4)})
+        return out
 
 
 def time_batch(launch, n: int) -> float:

@@ -179,6 +179,26 @@ def test_rows_disjoint_interleaved_heads_are_valid():
     assert _strides(t) == (128 * 2 * 64, 64, 128)
 
 
+def test_broadcast_row_has_no_stride_triple():
+    # a single row expanded to [B, H, N, d] has leading strides (0, 0, 0), the
+    # ABI's contiguous mark: inputs are copied, outputs rejected, and the
+    # stride helper never passes (0, 0, 0) for a non-contiguous tensor
+    import torch
+    from attention_attn_fwd_07_amd import _strides, _unbroadcast
+    row = torch.arange(64, dtype=torch.float32).reshape(1, 1, 1, 64)
+    t = row.expand(2, 3, 5, 64)
+    assert not t.is_contiguous() and tuple(t.stride()[:3]) == (0, 0, 0)
+    c = _unbroadcast(t, "k")
+    assert c.is_contiguous() and torch.equal(c, t) and _strides(c) == (0, 0, 0)
+    with pytest.raises(ValueError):
+        _unbroadcast(t, "o", output=True)
+    with pytest.raises(ValueError):
+        _strides(t)
+    # other views pass through unchanged
+    u = torch.zeros(1, 5, 2, 64).transpose(1, 2)
+    assert _unbroadcast(u, "q") is u
+
+
 def test_ex_strided_alias_uses_the_strided_extent(lib):
     # o written with BNHD strides spans 2*128*64 elements; an lse placed inside
     # that span is an alias even though it lies beyond o's first head.
@@ -189,6 +209,15 @@ def test_ex_strided_alias_uses_the_strided_extent(lib):
 def test_ex_head_bytes_limit(lib):
     # a head's rows must be addressable with 32-bit byte offsets in the kernels
     assert call_ex(lib, N=1 << 20, ks=(0, 0, 2048), d=64) == SHAPE
+
+
+@pytest.mark.parametrize("stride", [(1 << 63) // 6 // 8 * 8, (1 << 62) // 8 * 8 - 8,
+                                    (1 << 61) // 8 * 8])
+def test_ex_huge_row_stride_is_rejected(lib, stride):
+    # fp32, N = 2 and a row stride near INT64_MAX / 6: N * stride * 4 overflows
+    # int64; the head-bytes check must still reject it (no wrap past the bound)
+    code = call_ex(lib, B=1, H=1, N=2, d=64, dtype=F32, ks=(0, 0, stride))
+    assert code in (SHAPE, LAYOUT)
 
 
 # ---------------------------------------------------------------------------

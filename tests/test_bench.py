@@ -113,7 +113,10 @@ def test_short_window_gives_no_clock_fraction(tmp_path):
     with bench.ClockSampler(period_s=0.001, sysfs_dir=str(tmp_path)) as c:
         time.sleep(0.02)
     s = c.summary(achieved=1200.0, peak=2500.0)
-    assert s["sclk_mhz"] == 1100.0 and s["frac_at_clock"] is None and s["peak_at_clock"] is None
+    assert s["samples"] >= 1 and s["window_s"] < 0.25
+    for key in ("sclk_mhz", "sclk_mhz_min", "sclk_mhz_max", "power_w", "peak_at_clock",
+                "frac_at_clock"):
+        assert s[key] is None, key
 
 
 def test_step_counts_are_checked(capsys):

@@ -170,3 +170,35 @@ def test_binding_rejects_bad_strides():
     buf = torch.zeros(1, 2, 16, 68, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):  # row stride 68 is not a multiple of 8
         attn.fwd(buf[..., :64], q, q)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f16", 128), ("f32", 64)])
+def test_broadcast_key_row_gives_mean_of_v(dtype, d):
+    """K as one row broadcast over every (b, h, n) (all leading strides 0, the
+    form ``expand`` makes): every score of a row is equal, so O is the mean of
+    V's rows and lse = scale q.k0 + ln N (page 3 section 3's softmax of equal
+    scores).  The binding copies such an input to a contiguous tensor; the
+    result matches the oracle on the materialised keys."""
+    B, H, N = 2, 3, 300
+    q, k, v = datagen.make_qkv(B, H, N, d, dtype, seed=400 + d)
+    dev = torch.device("cuda:0")
+    k0 = k[:1, :1, :1].to(dev)
+    kb = k0.expand(B, H, N, d)
+    assert not kb.is_contiguous() and tuple(kb.stride()[:3]) == (0, 0, 0)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run(q.to(dev), kb, v.to(dev), scale)
+    o64 = o.cpu().double().numpy()
+    v64 = v.double().numpy()
+    tol = TOL[dtype]
+    assert np.abs(o64 - v64.mean(axis=2, keepdims=True)).max() <= tol["maxabs"]
+    k_full = k[:1, :1, :1].expand(B, H, N, d).contiguous()
+    o_ref, lse_ref = oracle.attention(q, k_full, v, scale)
+    check(o64, lse.cpu().double().numpy(), o_ref, lse_ref, dtype, f"broadcast k {dtype} d={d}")
+
+
+def test_broadcast_output_is_rejected():
+    attn = _attn()
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16, device="cuda").expand(1, 2, 16, 64)
+    with pytest.raises(ValueError):
+        attn.attn_fwd(q, q.clone(), q.clone(), o, None, 0.125)

@@ -232,12 +232,17 @@ __device__ __forceinline__ float tile_max16(const f32x16 (&s)[2], float c2) {
   return mt * c2;
 }
 
-// The reference max m (log2 domain) moves only when some row of the wave
-// exceeds it by more than this many doublings; until then P = 2^(t - m) may
-// reach 2^8, harmless in fp32 and in bf16/fp16 (same relative precision).
-// The result is the same softmax: O = acc / l with acc and l built from the
-// same reference.
-constexpr float kRescaleThreshold = 8.0f;
+// The reference max m (log2 domain) follows each row's running max exactly,
+// as in the pages' recurrence: whenever the tile's max of some row of the
+// wave exceeds that row's m, every row of the wave moves to max(m, m_tile)
+// and is rescaled (rows whose max did not move get alpha = 1 exactly).  A
+// tile that raises no row's max needs no rescale at all, which is the only
+// work skipped, and skipping it is exact.  Every P = 2^(t - m) is then at
+// most 1, and the key that sets a row's max gets P = 1 exactly, so the
+// 16-bit rounding of P (relative error up to 2^-8 for bf16) never touches
+// the key that dominates a row.  A lazier reference (moving only when the
+// max grows by several doublings) leaves such a key's P in (1, 2^k], rounded,
+// and on rows that one key dominates that rounding reaches the output whole.
 
 // Move each row's reference to max(m, m_tile) and rescale its l and
 // accumulator by 2^(m_old - m_new) (1 for rows whose reference stays).
@@ -255,25 +260,9 @@ __device__ __forceinline__ void rescale_to(float m_tile, float& m, float& l,
 template <int D>
 __device__ __forceinline__ void maybe_rescale(float m_tile, float& m, float& l,
                                               f32x16 (&acc)[Geo16<D>::DB]) {
-  if (__builtin_amdgcn_ballot_w64(m_tile > m + kRescaleThreshold) != 0)  // wave-uniform
+  if (__builtin_amdgcn_ballot_w64(m_tile > m) != 0)  // wave-uniform
     rescale_to<D>(m_tile, m, l, acc);
 }
-
-// Sum test, the cheaper alternative to the max test (used by the ping-pong
-// kernel on every tile that needs no mask): P is first formed against the
-// current reference m, without the tile's row max.  If every lane's sum of
-// its 32 probabilities is at most
-// 2^8, every P is at most 2^8 - the max test's bound - and the tile is done.
-// Otherwise the row max is taken, the rows are rescaled and P is formed
-// again.  The rare path runs whenever the max test would (and also for some
-// tiles whose max exceeds m by 3 to 8 doublings).  The limit is kept low on
-// purpose: a key that dominates its row then almost always moves the
-// reference to its own score, so its P is exactly 1 and loses nothing to the
-// 16-bit rounding of P; with a limit of 2^12 the rounding of such P (up to
-// 2^-9 relative for bf16) measurably raised the worst-case output error on
-// rows dominated by a few large scores.  The first tile always sets m from
-// its row max.
-constexpr float kSumLimit = 256.0f;
 
 // P = 2^(s * c2 - m), packed to the element type (RNE) as the B operand of
 // the P.V product; returns this lane's fp32 row-sum contribution (the
@@ -427,9 +416,6 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   float m = tile_max16(sA, c2);  // the first tile sets the reference exactly
   block_barrier();               // kbuf0 is free for K_2 only after every wave read K_0
 
-  // This kernel keeps the max test: the sum test's branch would split the
-  // block in which the compiler interleaves a tile's softmax with the next
-  // tile's MFMAs (measured slower here).
   auto body = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], const lds_u8* kb_next,
                   const lds_u8* vb_cur, lds_u8* kb_load, lds_u8* vb_load) {
     const int j1 = J(t + 1);
@@ -625,24 +611,6 @@ __device__ __forceinline__ void mfma_phase(const lds_u8* lsm, uint32_t kbo, uint
   __builtin_amdgcn_s_setprio(0);
 }
 
-// S = K Q^T over one 64-key K tile (LDS byte offset kbo) alone: the rare
-// path of the sum test forms S again rather than keeping it live.
-template <class E, int D>
-__device__ __forceinline__ void qk_tile(const lds_u8* lsm, uint32_t kbo, LdsLanes<D> ln,
-                                        const u32x4 (&qf)[Geo16<D>::KS], f32x16 (&s)[2]) {
-  using G = Geo16<D>;
-  const uint32_t kqb = ln.kq + kbo;
-  s[0] = (f32x16){};
-  s[1] = (f32x16){};
-#pragma unroll
-  for (int ks = 0; ks < G::KS; ++ks) {
-    const lds_u8* ka = lsm + (kqb ^ (uint32_t)(ks << 5));
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-      s[sb] = E::mfma(*(const lds_u32x4*)(ka + sb * 32 * G::ROWB), qf[ks], s[sb]);
-  }
-}
-
 // Tile loads of the ping-pong kernel, issued by the four waves of one group.
 // One buffer descriptor per tile and tensor: its base is the tile's first row
 // and its size covers only the tile's rows below N, so the hardware range
@@ -685,8 +653,8 @@ struct PPLoader {
 // 8 waves = 256 query rows per block, in two groups of 4 waves; waves w and
 // w + 4 run on the same SIMD.  Per key tile each wave has an MFMA phase
 // (acc += P_{t-1} V_{t-1}, then S_t = K_t Q^T: 2 x 16 MFMAs) and a VALU phase
-// (row max, rare rescale, P_t = 2^(t - m), row sum).  Execution proceeds in
-// barrier-separated slots; group 1 runs one slot behind group 0, so in every
+// (row max, rescale if a row max moved, P_t = 2^(t - m), row sum).  Slots are
+// separated by barriers; group 1 runs one slot behind group 0, so in every
 // slot one wave of each SIMD issues MFMAs while the other issues the VALU
 // work that the MFMA pipe cannot do, instead of both competing for the same
 // unit at the same time.
@@ -697,8 +665,7 @@ struct PPLoader {
 // 1's.
 //
 // K and V tiles stream through four-deep LDS rings (tile t in ring slot
-// t % 4).  Each group loads one tensor, right after its MFMA phase, where the
-// wave's issue port has slack (the VALU phases are the longer ones):
+// t % 4).  Each group loads one tensor, right after its MFMA phase:
 //   * group 0, after the MFMA phase of tile t (slot 2t), loads V_{t+2}, which
 //     overwrites V_{t-2}; it awaits V_t at the end of its VALU phase of tile
 //     t (slot 2t + 1), in time for the MFMA phase of tile t + 1;
@@ -709,7 +676,9 @@ struct PPLoader {
 // (slots 2t - 2 and 2t - 1).  Each load has about four slots to arrive: the
 // query blocks of a head stream the same tiles at about the same time, and
 // the first of them to ask for a tile pays the full memory latency.  K_0..K_2
-// and V_0, V_1 are loaded before the first slot.
+// and V_0, V_1 are loaded before the first slot.  (Issuing the loads at the
+// start of the VALU phase instead, where that phase has slack, measured 1-2 %
+// slower.)
 constexpr int kPPThreads = 512;
 constexpr int kRing = 4;
 
@@ -811,19 +780,11 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const uint32_t vbo = VRING + (uint32_t)((t + kRing - 1) % kRing) * TB;
     mfma_phase<E, D>(lsm, kbo, vbo, ln, t > 0, pb, acc, qf, sc);
   };
-  // VALU phase of tile t.
-  // The rare path forms S again from K_t, which stays in its ring slot until
-  // both groups have finished the VALU phase of tile t.
-  // Full tiles take the sum test; the causal kernel's diagonal tiles keep the
-  // max test (its masking code leaves no registers for the second pass).
-  auto valu_full = [&](int t) __attribute__((always_inline)) {
-    float ps = softmax16<E, false>(sc, m, c2, pb, 0, 0);
-    if (__builtin_amdgcn_ballot_w64(ps > kSumLimit) != 0) {  // rare; wave-uniform
-      qk_tile<E, D>(lsm, (uint32_t)(t % kRing) * TB, ln, qf, sc);
-      rescale_to<D>(tile_max16(sc, c2), m, l, acc);
-      ps = softmax16<E, false>(sc, m, c2, pb, 0, 0);
-    }
-    l += ps;
+  // VALU phase of tile t: row max, rescale where some row's max moved, then
+  // P and the row sums.  Tiles that need no mask skip the compares.
+  auto valu_full = [&]() __attribute__((always_inline)) {
+    maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
+    l += softmax16<E, false>(sc, m, c2, pb, 0, 0);
   };
   // The first tile sets the reference from its row max (m = -inf before).
   auto valu_first = [&]() __attribute__((always_inline)) {
@@ -839,22 +800,11 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   auto valu_any = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * G::BN;
     if (kl.partial(j0, G::BN)) {
-      if (CAUSAL) {
-        mask_tail16(sc, j0, kl.lane_lim, c2);
-        maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
-        l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
-        return;
-      }
-      float ps = softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
-      if (__builtin_amdgcn_ballot_w64(ps > kSumLimit) != 0) {
-        qk_tile<E, D>(lsm, (uint32_t)(t % kRing) * TB, ln, qf, sc);
-        mask_tail16(sc, j0, kl.lane_lim, c2);
-        rescale_to<D>(tile_max16(sc, c2), m, l, acc);
-        ps = softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
-      }
-      l += ps;
+      mask_tail16(sc, j0, kl.lane_lim, c2);
+      maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
+      l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
     } else {
-      valu_full(t);
+      valu_full();
     }
   };
   // Tiles between the first and the last: all full without a causal mask;
@@ -863,7 +813,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (CAUSAL)
       valu_any(t);
     else
-      valu_full(t);
+      valu_full();
   };
   auto pv_last = [&]() __attribute__((always_inline)) {
     uint32_t vq = ln.vq;
@@ -914,9 +864,9 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   } else {
     static_assert(kPPThreads / 64 * 32 * 2 * D <= kRing * G::TILEB,
                   "the output staging must fit in the K ring");
-    // The K ring is free here: its last reader, the VALU phase of the last
-    // tile (whose rare path may form S again from K), ended at this wave's
-    // last barrier, and every tile load has landed.  Wave w takes bytes
+    // The K ring is free here: its last reader, the MFMA phase of the last
+    // tile, ended before this wave's last barrier, and every tile load has
+    // landed.  Wave w takes bytes
     // w * 32 * 2D .. of it (8 waves x 8 KiB = the 4 K slots at d = 128).
     store_rows_lds<E, D>((lds_u8*)smem + wave * 32 * 2 * D, Oh, LSE, L, bh, N,
                          qt * BM + wave * 32, acc, inv, lse);
@@ -1387,10 +1337,10 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
   int nsplit = 1;
   if (splits != 0) {
     split_plan(N, splits, &split_len, &nsplit);
-    if (ws == nullptr) return ATTN_ERR_NULLPTR;
-    if (misaligned(ws, 16)) return ATTN_ERR_ALIGN;
     int64_t need = 0;
     if (!mul_ok(bhn, (d + 1) * 4, &need) || !mul_ok(need, nsplit, &need)) return ATTN_ERR_SHAPE;
+    if (ws == nullptr) return ATTN_ERR_NULLPTR;
+    if (misaligned(ws, 16)) return ATTN_ERR_ALIGN;
     if (ws_bytes < (uint64_t)need) return ATTN_ERR_WORKSPACE;
     const uintptr_t w0 = reinterpret_cast<uintptr_t>(ws), w1 = w0 + (size_t)need;
     for (int t = 0; t < 4; ++t)

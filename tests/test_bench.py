@@ -73,7 +73,11 @@ def test_bench_json_line(extra, capsys):
     assert d["value"] > 0 and d["ms_per_step"] > 0
     c = d["clock"]  # None where the driver's sysfs files are not readable
     if c is not None:
-        assert c["samples"] >= 1 and 0 < c["sclk_mhz"] <= 3000
+        assert c["samples"] >= 1
+        if c["window_s"] < 0.25:  # a few launches: nothing measured is reported
+            assert c["sclk_mhz"] is None and c["power_w"] is None and c["frac_at_clock"] is None
+        else:
+            assert 0 < c["sclk_mhz"] <= 3000
         if c["frac_at_clock"] is not None:
             assert math.isclose(c["frac_at_clock"], r["achieved"] / c["peak_at_clock"],
                                 rel_tol=1e-2)

@@ -10,6 +10,7 @@ GPU is present, calls raise.
     attn_fwd(q, k, v, o, lse, scale)       # caller-owned outputs, async launch
     p = plan(q, k, v, o, lse, scale); p()  # checked once, then relaunched cheaply
     o, lse = fwd_splitkv(q, k, v, splits=8)  # keys split over 8 blocks, then merged
+    attn_fwd_splitkv_static(q, k, v, o, lse, scale, 4)  # no workspace, no allocation
     dq, dk, dv = bwd(q, k, v, o, lse, do)    # gradients (include/attn_bwd.h)
 
 Tensors are ``[B, H, N, d]`` fp32/fp16/bf16 with d in {64, 128}; the head
@@ -31,7 +32,9 @@ from .build import LIB
 
 __all__ = ["attn_fwd", "fwd", "plan", "Plan", "attn_strerror", "attn_version", "library_path",
            "AttnError", "ATTN_CAUSAL", "splitkv_workspace_size", "fwd_splitkv", "attn_bwd",
-           "bwd", "bwd_workspace_size"]
+           "bwd", "bwd_workspace_size", "attn_fwd_splitkv_static", "STATIC_WORKSPACE_BYTES"]
+
+STATIC_WORKSPACE_BYTES = 64 << 20  # ATTN_STATIC_WORKSPACE_BYTES of include/attn_fwd.h
 
 ATTN_OK = 0
 ATTN_ERR_HIP = -8
@@ -94,6 +97,8 @@ def _load():
     lib.attn_fwd_ex.restype = ctypes.c_int
     lib.attn_fwd_splitkv.argtypes = [ctypes.POINTER(_Args), ctypes.c_int, vp, ctypes.c_size_t]
     lib.attn_fwd_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_splitkv_static.argtypes = [ctypes.POINTER(_Args), ctypes.c_int]
+    lib.attn_fwd_splitkv_static.restype = ctypes.c_int
     lib.attn_fwd_splitkv_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.attn_fwd_splitkv_workspace.restype = ctypes.c_size_t
     lib.attn_bwd.argtypes = [ctypes.POINTER(_BwdArgs), vp, ctypes.c_size_t]
@@ -202,7 +207,7 @@ class Plan:
     """
 
     def __init__(self, q, k, v, o, lse, scale: float, stream=None, causal: bool = False,
-                 splits: int = 0, workspace=None):
+                 splits: int = 0, workspace=None, static_workspace: bool = False):
         torch = _torch()
         code_dtype = _check(q, k, v, o, lse)
         q, k, v = (_unbroadcast(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v")))
@@ -228,7 +233,12 @@ class Plan:
         a.stream = stream
         self._args = a
         self._ref = ctypes.byref(a)
-        if splits:
+        if splits and static_workspace:
+            if workspace is not None:
+                raise ValueError("the static split-KV path takes no workspace")
+            fn = lib.attn_fwd_splitkv_static
+            self._call = lambda: fn(self._ref, int(splits))
+        elif splits:
             if workspace is None:
                 raise ValueError("the split-KV path needs a workspace tensor")
             if workspace.device != q.device or not workspace.is_contiguous():
@@ -283,6 +293,20 @@ def fwd_splitkv(q, k, v, scale: float | None = None, splits: int = 4, workspace=
         with torch.cuda.device(p.device):
             p()
     return o, lse
+
+
+def attn_fwd_splitkv_static(q, k, v, o, lse, scale: float, splits: int, stream=None) -> None:
+    """``attn_fwd_splitkv`` into the caller's ``o`` and ``lse`` with the
+    library's own static device workspace (ATTN_STATIC_WORKSPACE_BYTES): the
+    library allocates nothing.  Calls on one device share that workspace, so
+    overlapping calls (different streams) race; order them on one stream."""
+    torch = _torch()
+    p = Plan(q, k, v, o, lse, scale, stream, False, splits, None, static_workspace=True)
+    if torch.cuda.current_device() == p.device.index:
+        p()
+    else:
+        with torch.cuda.device(p.device):
+            p()
 
 
 def attn_fwd(q, k, v, o, lse, scale: float, stream=None, causal: bool = False) -> None:

@@ -50,6 +50,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "attn_common.h"
 #include "attn_fwd.h"
 
@@ -1265,8 +1267,42 @@ void split_plan(int64_t N, int requested, int64_t* len, int* splits) {
   *splits = (int)((tiles + per - 1) / per);
 }
 
-// The plain path (splits == 0), or the split-KV path with its workspace.
-int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t ws_bytes = 0) {
+}  // namespace
+
+// The workspace of attn_fwd_splitkv_static: fp32 partial outputs and
+// log-sum-exps between the split-KV kernel and the merge, in a library-owned
+// device array (each device that runs the library holds its own copy until
+// the process ends).  In host code `scratch` names a host-side stand-in, not
+// device memory: only the address hipGetSymbolAddress returns for the
+// current device may be handed to kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) and kept.
+int static_workspace(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+// The plain path (splits == 0), or the split-KV path with its workspace: the
+// caller's (ws, ws_bytes), or with static_ws the library's own array.
+int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t ws_bytes = 0,
+            bool static_ws = false) {
   // --- validation: no HIP call before this block has passed -------------
   const int64_t B = a.B, H = a.H, N = a.N, d = a.d;
   if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
@@ -1339,6 +1375,13 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
     split_plan(N, splits, &split_len, &nsplit);
     int64_t need = 0;
     if (!mul_ok(bhn, (d + 1) * 4, &need) || !mul_ok(need, nsplit, &need)) return ATTN_ERR_SHAPE;
+    if (static_ws) {
+      // the size limit is checked before the first HIP call of this path
+      if ((uint64_t)need > ATTN_STATIC_WORKSPACE_BYTES) return ATTN_ERR_STATIC_LIMIT;
+      const int rc = static_workspace(&ws);
+      if (rc != ATTN_OK) return rc;
+      ws_bytes = ATTN_STATIC_WORKSPACE_BYTES;
+    }
     if (ws == nullptr) return ATTN_ERR_NULLPTR;
     if (misaligned(ws, 16)) return ATTN_ERR_ALIGN;
     if (ws_bytes < (uint64_t)need) return ATTN_ERR_WORKSPACE;
@@ -1422,6 +1465,12 @@ extern "C" int attn_fwd_splitkv(const attn_fwd_args_t* args, int splits, void* w
   return run_fwd(*args, splits, workspace, workspace_bytes);
 }
 
+extern "C" int attn_fwd_splitkv_static(const attn_fwd_args_t* args, int splits) {
+  if (args == nullptr) return ATTN_ERR_NULLPTR;
+  if (splits < 1 || splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
+  return run_fwd(*args, splits, nullptr, 0, true);
+}
+
 extern "C" const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";
@@ -1437,6 +1486,7 @@ extern "C" const char* attn_strerror(int code) {
     case ATTN_ERR_SPLITS: return "split count out of range (1 .. ATTN_MAX_SPLITS)";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_fwd_splitkv_workspace()";
     case ATTN_ERR_LAYOUT: return "invalid strides: negative, not a multiple of 8 elements, or overlapping output rows";
+    case ATTN_ERR_STATIC_LIMIT: return "the split-KV partial results exceed the library's static workspace (ATTN_STATIC_WORKSPACE_BYTES)";
     default: return "unknown error code";
   }
 }

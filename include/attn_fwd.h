@@ -53,7 +53,9 @@ enum {
   ATTN_ERR_LAYOUT = -10,  /* attn_fwd_ex: a stride is negative, not a multiple
                              of 8 elements, or rows of a head overlap           */
   ATTN_ERR_SPLITS = -11,  /* attn_fwd_splitkv: splits not in 1..ATTN_MAX_SPLITS */
-  ATTN_ERR_WORKSPACE = -12 /* attn_fwd_splitkv: workspace_bytes too small       */
+  ATTN_ERR_WORKSPACE = -12, /* attn_fwd_splitkv: workspace_bytes too small      */
+  ATTN_ERR_STATIC_LIMIT = -13 /* attn_fwd_splitkv_static: the partial results need
+                                 more than ATTN_STATIC_WORKSPACE_BYTES          */
 };
 
 /* Largest split count of attn_fwd_splitkv. */
@@ -170,6 +172,37 @@ int attn_fwd_splitkv(const attn_fwd_args_t* args, int splits, void* workspace,
 /* Bytes of workspace attn_fwd_splitkv needs (splits_used * B*H*N * (d + 1)
  * * 4), or 0 for empty or invalid sizes. */
 size_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d, int splits);
+
+/* Size of the library's own device array behind attn_fwd_splitkv_static. */
+#define ATTN_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/*
+ * attn_fwd_splitkv_static - attn_fwd_splitkv without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, serving loops and harnesses that forbid
+ * hipMalloc.
+ *
+ * The fp32 partial results live in a static device array of
+ * ATTN_STATIC_WORKSPACE_BYTES (64 MiB) that the library owns; every device
+ * the library runs on holds its own copy from the first call on it until the
+ * process ends.  The call allocates and frees nothing (no hipMalloc, no
+ * allocating library routine); on its first call on a device it looks the
+ * array's address up (hipGetSymbolAddress) with that device current.
+ *
+ * args, splits : as for attn_fwd_splitkv (the same kernels run, so the result
+ *                is bit-identical to attn_fwd_splitkv with the same splits).
+ * Returns the codes of attn_fwd_splitkv, minus the workspace ones, plus
+ * ATTN_ERR_STATIC_LIMIT when attn_fwd_splitkv_workspace(B, H, N, d, splits)
+ * exceeds ATTN_STATIC_WORKSPACE_BYTES; that and every other argument error is
+ * detected before any HIP call.
+ *
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents.  Nothing in it has to start at zero: the first kernel
+ * writes every partial row the merge reads.  Calls that overlap in time on
+ * one device (different streams, or different host threads without ordering)
+ * race on the array and give wrong results; order them on one stream.
+ */
+int attn_fwd_splitkv_static(const attn_fwd_args_t* args, int splits);
 
 /* Static text for a return code (never NULL). */
 const char* attn_strerror(int code);

@@ -267,6 +267,36 @@ def test_splitkv_rejects_before_any_hip_call(lib, kw, code):
     assert call_split(lib, **kw) == code
 
 
+STATIC_LIMIT = -13
+# fake tensors far apart, for shapes whose extents exceed the 1 MiB spacing above
+FAR = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40)
+
+
+def call_static(lib, splits=4, **kw):
+    from attention_attn_fwd_07_amd import _Args
+    lib.attn_fwd_splitkv_static.argtypes = [ctypes.POINTER(_Args), ctypes.c_int]
+    lib.attn_fwd_splitkv_static.restype = ctypes.c_int
+    return lib.attn_fwd_splitkv_static(ctypes.byref(ex_args(**kw)), splits)
+
+
+@pytest.mark.parametrize("kw,code", [
+    # the partial results of 8 splits of 64 x 65536 rows are far beyond 64 MiB
+    (dict(B=1, H=64, N=65536, d=128, splits=8, **FAR), STATIC_LIMIT),
+    (dict(B=1, H=64, N=1024, d=128, splits=3, **FAR), STATIC_LIMIT),   # 101 MB
+    (dict(splits=0), SPLITS), (dict(splits=65), SPLITS), (dict(flags=1), FLAGS),
+    (dict(d=96), HEAD_DIM), (dict(q=None), NULLPTR), (dict(o=Q), ALIAS),
+    (dict(N=0), OK),
+])
+def test_splitkv_static_rejects_before_any_hip_call(lib, kw, code):
+    assert call_static(lib, **kw) == code
+
+
+def test_splitkv_static_null_args(lib):
+    lib.attn_fwd_splitkv_static.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.attn_fwd_splitkv_static.restype = ctypes.c_int
+    assert lib.attn_fwd_splitkv_static(None, 2) == NULLPTR
+
+
 # ---------------------------------------------------------------------------
 # attn_bwd: argument checks
 # ---------------------------------------------------------------------------

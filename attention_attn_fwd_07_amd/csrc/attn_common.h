@@ -42,6 +42,11 @@ struct Bf16T {
   static __device__ __forceinline__ u32 pack2(float lo, float hi) {
     return __builtin_bit_cast(u32, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
   }
+  // acc + the two bf16 values packed in w, in fp32 (v_dot2c_f32_bf16 with 1, 1).
+  static __device__ __forceinline__ float sum2(u32 w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+  }
 };
 
 struct F16T {
@@ -52,6 +57,11 @@ struct F16T {
   // Two fp32 -> two fp16, round to nearest even.
   static __device__ __forceinline__ u32 pack2(float lo, float hi) {
     return __builtin_bit_cast(u32, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+  }
+  // acc + the two fp16 values packed in w, in fp32 (v_dot2c_f32_f16 with 1, 1).
+  static __device__ __forceinline__ float sum2(u32 w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                  (f16x2){(_Float16)1.0f, (_Float16)1.0f}, acc, false);
   }
 };
 

@@ -234,22 +234,27 @@ __device__ __forceinline__ float tile_max16(const f32x16 (&s)[2], float c2) {
   return mt * c2;
 }
 
-// The reference max m (log2 domain) follows each row's running max exactly,
-// as in the pages' recurrence: whenever the tile's max of some row of the
-// wave exceeds that row's m, every row of the wave moves to max(m, m_tile)
-// and is rescaled (rows whose max did not move get alpha = 1 exactly).  A
-// tile that raises no row's max needs no rescale at all, which is the only
-// work skipped, and skipping it is exact.  Every P = 2^(t - m) is then at
-// most 1, and the key that sets a row's max gets P = 1 exactly, so the
-// 16-bit rounding of P (relative error up to 2^-8 for bf16) never touches
-// the key that dominates a row.  A lazier reference (moving only when the
-// max grows by several doublings) leaves such a key's P in (1, 2^k], rounded,
-// and on rows that one key dominates that rounding reaches the output whole.
+// The reference max m (log2 domain) moves only when some row of the wave
+// exceeds it by more than this many doublings; until then P = 2^(t - m) may
+// reach 2^8, harmless in fp32 and in bf16/fp16 (same relative precision).
+// The result is the same softmax: O = acc / l with acc and l built from the
+// same reference.  A key that dominates its row may then keep a P in
+// (1, 2^8] that is no power of two, and the 16-bit rounding of that P (up to
+// 2^-8 relative for bf16) enters acc; the ping-pong kernel, which uses this
+// threshold, therefore normalises O by the sum of the same rounded P (l[1]
+// below), so the weights applied to V sum to one exactly and that rounding
+// cancels between numerator and denominator, while the log-sum-exp uses the
+// sum of the unrounded P (l[0]).  The pipelined kernel instead follows the
+// exact running max (threshold 0: every P is at most 1 and the key that sets
+// a row's max has P = 1 exactly) and normalises by l[0]; at d = 64 its VALU
+// work sets its speed, and the rare extra rescales of long rows cost less
+// than the rounded sum would.
+constexpr float kRescaleThreshold = 8.0f;
 
 // Move each row's reference to max(m, m_tile) and rescale its l and
 // accumulator by 2^(m_old - m_new) (1 for rows whose reference stays).
 template <int D>
-__device__ __forceinline__ void rescale_to(float m_tile, float& m, float& l,
+__device__ __forceinline__ void rescale_to(float m_tile, float& m, f32x2& l,
                                            f32x16 (&acc)[Geo16<D>::DB]) {
   const float m_new = fmaxf(m, m_tile);
   const float alpha = fast_exp2(m - m_new);
@@ -259,18 +264,33 @@ __device__ __forceinline__ void rescale_to(float m_tile, float& m, float& l,
   for (int db = 0; db < Geo16<D>::DB; ++db) acc[db] *= alpha;
 }
 
+// Rescale when some row's tile max exceeds its reference by more than thr
+// doublings: kRescaleThreshold with the rounded-sum normalisation, 0 (the
+// exact running max) without it.
 template <int D>
-__device__ __forceinline__ void maybe_rescale(float m_tile, float& m, float& l,
-                                              f32x16 (&acc)[Geo16<D>::DB]) {
-  if (__builtin_amdgcn_ballot_w64(m_tile > m) != 0)  // wave-uniform
+__device__ __forceinline__ void maybe_rescale(float m_tile, float& m, f32x2& l,
+                                              f32x16 (&acc)[Geo16<D>::DB], float thr) {
+  if (__builtin_amdgcn_ballot_w64(m_tile > m + thr) != 0)  // wave-uniform
     rescale_to<D>(m_tile, m, l, acc);
 }
 
+// Sum test, the cheaper alternative to the max test (used by the ping-pong
+// kernel on every tile that needs no mask): P is first formed against the
+// current reference m, without the tile's row max.  If every lane's sum of
+// its 32 probabilities is at most 2^8, every P is at most 2^8 - the max
+// test's bound - and the tile is done.  Otherwise the row max is taken, the
+// rows are rescaled and P is formed again.  The rare path runs whenever the
+// max test would (and also for some tiles whose max exceeds m by 3 to 8
+// doublings).  The first tile always sets m from its row max.
+constexpr float kSumLimit = 256.0f;
+
 // P = 2^(s * c2 - m), packed to the element type (RNE) as the B operand of
-// the P.V product; returns this lane's fp32 row-sum contribution (the
-// log-sum-exp output depends on it directly, so it sums unrounded values).
-template <class E, bool TAIL>
-__device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float c2,
+// the P.V product.  Returns this lane's two row-sum contributions: [0] of the
+// fp32 P (for the log-sum-exp, which depends on it directly) and [1] of the
+// rounded P the product uses (for normalising O), the latter two packed
+// values per v_dot2c against (1, 1).
+template <class E, bool TAIL, bool RSUM = true>
+__device__ __forceinline__ f32x2 softmax16(const f32x16 (&s)[2], float m, float c2,
                                            u32x4 (&pb)[2][2], int j0, int lim) {
   const int hh = (threadIdx.x & 63) >> 5;
   // Eight independent partial sums: a single running sum would be a chain
@@ -297,7 +317,18 @@ __device__ __forceinline__ float softmax16(const f32x16 (&s)[2], float m, float 
                            E::pack2(p[b0 + 4], p[b0 + 5]), E::pack2(p[b0 + 6], p[b0 + 7])};
     }
   }
-  return ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+  const float sum =
+      ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+  if (!RSUM) return (f32x2){sum, 0.f};
+  // Sums of the rounded P: two chains of eight pair sums.
+  float rp[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) rp[c] = E::sum2(pb[c][0][0], 0.f);
+#pragma unroll
+  for (int w = 1; w < 8; ++w)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) rp[c] = E::sum2(pb[c][w >> 2][w & 3], rp[c]);
+  return (f32x2){sum, rp[0] + rp[1]};
 }
 
 // O^T += V^T P^T, 16 keys per MFMA; V^T comes from transposing LDS reads:
@@ -407,7 +438,7 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   f32x16 acc[G::DB];
 #pragma unroll
   for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
-  float l = 0.f;
+  f32x2 l = (f32x2){0.f, 0.f};  // row sum of the fp32 P ([1] unused here)
 
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   block_barrier();
@@ -418,6 +449,9 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   float m = tile_max16(sA, c2);  // the first tile sets the reference exactly
   block_barrier();               // kbuf0 is free for K_2 only after every wave read K_0
 
+  // This kernel keeps the max test: the sum test's branch would split the
+  // block in which the compiler interleaves a tile's softmax with the next
+  // tile's MFMAs (measured slower here).
   auto body = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], const lds_u8* kb_next,
                   const lds_u8* vb_cur, lds_u8* kb_load, lds_u8* vb_load) {
     const int j1 = J(t + 1);
@@ -425,13 +459,13 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (j1 < Nk) loader.load_v(Vb, j1, Nk, vb_load);
     u32x4 pb[2][2];
     if (CAUSAL && kl.partial(J(t), G::BN))  // a diagonal tile (others are full)
-      l += softmax16<E, true>(cur, m, c2, pb, J(t), kl.lane_lim);
+      l += softmax16<E, true, false>(cur, m, c2, pb, J(t), kl.lane_lim);
     else
-      l += softmax16<E, false>(cur, m, c2, pb, 0, 0);
+      l += softmax16<E, false, false>(cur, m, c2, pb, 0, 0);
     qk16<E, D>(kb_next, qf, nxt);
     pv16<E, D>(vb_cur, pb, acc);
     if (kl.partial(j1, G::BN)) mask_tail16(nxt, j1, kl.lane_lim, c2);
-    maybe_rescale<D>(tile_max16(nxt, c2), m, l, acc);
+    maybe_rescale<D>(tile_max16(nxt, c2), m, l, acc, 0.f);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads landed
     block_barrier();                                     // ... and everyone's
   };
@@ -442,9 +476,9 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // (a zero P times unloaded LDS could still make NaN), so nothing to add
     if (KS2 == 2 && j0 >= Nk) return;
     if (kl.partial(j0, G::BN))
-      l += softmax16<E, true>(cur, m, c2, pb, j0, kl.lane_lim);
+      l += softmax16<E, true, false>(cur, m, c2, pb, j0, kl.lane_lim);
     else
-      l += softmax16<E, false>(cur, m, c2, pb, j0, 0);
+      l += softmax16<E, false, false>(cur, m, c2, pb, j0, 0);
     pv16<E, D>(vb_cur, pb, acc);
   };
 
@@ -461,7 +495,7 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     last(t, sA, vbuf0);
   }
 
-  constexpr int NV = G::DB * 16 + 2;  // floats per lane in the key-split merge
+  constexpr int NV = G::DB * 16 + 3;  // floats per lane in the key-split merge
   if (KS2 == 2) {
     // Merge the two halves' states through LDS (the K/V buffers are free once
     // every wave is past its last PV product).  Half 1 writes its m, l and
@@ -475,24 +509,28 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
         for (int r = 0; r < 16; ++r) xs[db * 16 + r] = acc[db][r];
       xs[G::DB * 16] = m;
-      xs[G::DB * 16 + 1] = l;
+      xs[G::DB * 16 + 1] = l[0];
+      xs[G::DB * 16 + 2] = l[1];
     }
     block_barrier();
     if (kh == 1) return;
-    const float m1 = xs[G::DB * 16], l1 = xs[G::DB * 16 + 1];
-    const bool has1 = xhalf_sum(l1) > 0.f;
+    const float m1 = xs[G::DB * 16];
+    const f32x2 l1 = (f32x2){xs[G::DB * 16 + 1], xs[G::DB * 16 + 2]};
+    const bool has1 = xhalf_sum(l1[0]) > 0.f;
     const float mn = has1 ? fmaxf(m, m1) : m;
     const float a0 = fast_exp2(m - mn), a1 = has1 ? fast_exp2(m1 - mn) : 0.f;
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * a0 + (has1 ? xs[db * 16 + r] * a1 : 0.f);
-    l = l * a0 + (has1 ? l1 * a1 : 0.f);
+    l = l * a0 + (has1 ? l1 * a1 : (f32x2){0.f, 0.f});
     m = mn;
   }
 
   // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.
-  const float lt = xhalf_sum(l);
+  // This kernel keeps the exact running max (threshold 0), so every P is at
+  // most 1 and a row's dominant key has P = 1 exactly: no rounded sum needed.
+  const float lt = xhalf_sum(l[0]);
   const float inv = 1.0f / lt;
   const float lse = (m + log2f(lt)) * kLn2;
   if (sp.len) {
@@ -613,6 +651,24 @@ __device__ __forceinline__ void mfma_phase(const lds_u8* lsm, uint32_t kbo, uint
   __builtin_amdgcn_s_setprio(0);
 }
 
+// S = K Q^T over one 64-key K tile (LDS byte offset kbo) alone: the rare
+// path of the sum test forms S again rather than keeping it live.
+template <class E, int D>
+__device__ __forceinline__ void qk_tile(const lds_u8* lsm, uint32_t kbo, LdsLanes<D> ln,
+                                        const u32x4 (&qf)[Geo16<D>::KS], f32x16 (&s)[2]) {
+  using G = Geo16<D>;
+  const uint32_t kqb = ln.kq + kbo;
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) {
+    const lds_u8* ka = lsm + (kqb ^ (uint32_t)(ks << 5));
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+      s[sb] = E::mfma(*(const lds_u32x4*)(ka + sb * 32 * G::ROWB), qf[ks], s[sb]);
+  }
+}
+
 // Tile loads of the ping-pong kernel, issued by the four waves of one group.
 // One buffer descriptor per tile and tensor: its base is the tile's first row
 // and its size covers only the tile's rows below N, so the hardware range
@@ -655,8 +711,8 @@ struct PPLoader {
 // 8 waves = 256 query rows per block, in two groups of 4 waves; waves w and
 // w + 4 run on the same SIMD.  Per key tile each wave has an MFMA phase
 // (acc += P_{t-1} V_{t-1}, then S_t = K_t Q^T: 2 x 16 MFMAs) and a VALU phase
-// (row max, rescale if a row max moved, P_t = 2^(t - m), row sum).  Slots are
-// separated by barriers; group 1 runs one slot behind group 0, so in every
+// (row max, rare rescale, P_t = 2^(t - m), row sum).  Execution proceeds in
+// barrier-separated slots; group 1 runs one slot behind group 0, so in every
 // slot one wave of each SIMD issues MFMAs while the other issues the VALU
 // work that the MFMA pipe cannot do, instead of both competing for the same
 // unit at the same time.
@@ -667,7 +723,8 @@ struct PPLoader {
 // 1's.
 //
 // K and V tiles stream through four-deep LDS rings (tile t in ring slot
-// t % 4).  Each group loads one tensor, right after its MFMA phase:
+// t % 4).  Each group loads one tensor, right after its MFMA phase, where the
+// wave's issue port has slack (the VALU phases are the longer ones):
 //   * group 0, after the MFMA phase of tile t (slot 2t), loads V_{t+2}, which
 //     overwrites V_{t-2}; it awaits V_t at the end of its VALU phase of tile
 //     t (slot 2t + 1), in time for the MFMA phase of tile t + 1;
@@ -678,9 +735,7 @@ struct PPLoader {
 // (slots 2t - 2 and 2t - 1).  Each load has about four slots to arrive: the
 // query blocks of a head stream the same tiles at about the same time, and
 // the first of them to ask for a tile pays the full memory latency.  K_0..K_2
-// and V_0, V_1 are loaded before the first slot.  (Issuing the loads at the
-// start of the VALU phase instead, where that phase has slack, measured 1-2 %
-// slower.)
+// and V_0, V_1 are loaded before the first slot.
 constexpr int kPPThreads = 512;
 constexpr int kRing = 4;
 
@@ -757,7 +812,8 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   f32x16 acc[G::DB];
 #pragma unroll
   for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY;
+  f32x2 l = (f32x2){0.f, 0.f};  // row sums of the fp32 P and of the rounded P
   f32x16 sc[2];
   u32x4 pb[2][2];
 #pragma unroll
@@ -782,11 +838,19 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const uint32_t vbo = VRING + (uint32_t)((t + kRing - 1) % kRing) * TB;
     mfma_phase<E, D>(lsm, kbo, vbo, ln, t > 0, pb, acc, qf, sc);
   };
-  // VALU phase of tile t: row max, rescale where some row's max moved, then
-  // P and the row sums.  Tiles that need no mask skip the compares.
-  auto valu_full = [&]() __attribute__((always_inline)) {
-    maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
-    l += softmax16<E, false>(sc, m, c2, pb, 0, 0);
+  // VALU phase of tile t.
+  // The rare path forms S again from K_t, which stays in its ring slot until
+  // both groups have finished the VALU phase of tile t.
+  // Full tiles take the sum test; the causal kernel's diagonal tiles keep the
+  // max test (its masking code leaves no registers for the second pass).
+  auto valu_full = [&](int t) __attribute__((always_inline)) {
+    f32x2 ps = softmax16<E, false>(sc, m, c2, pb, 0, 0);
+    if (__builtin_amdgcn_ballot_w64(ps[0] > kSumLimit) != 0) {  // rare; wave-uniform
+      qk_tile<E, D>(lsm, (uint32_t)(t % kRing) * TB, ln, qf, sc);
+      rescale_to<D>(tile_max16(sc, c2), m, l, acc);
+      ps = softmax16<E, false>(sc, m, c2, pb, 0, 0);
+    }
+    l += ps;
   };
   // The first tile sets the reference from its row max (m = -inf before).
   auto valu_first = [&]() __attribute__((always_inline)) {
@@ -802,11 +866,22 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   auto valu_any = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * G::BN;
     if (kl.partial(j0, G::BN)) {
-      mask_tail16(sc, j0, kl.lane_lim, c2);
-      maybe_rescale<D>(tile_max16(sc, c2), m, l, acc);
-      l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+      if (CAUSAL) {
+        mask_tail16(sc, j0, kl.lane_lim, c2);
+        maybe_rescale<D>(tile_max16(sc, c2), m, l, acc, kRescaleThreshold);
+        l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+        return;
+      }
+      f32x2 ps = softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+      if (__builtin_amdgcn_ballot_w64(ps[0] > kSumLimit) != 0) {
+        qk_tile<E, D>(lsm, (uint32_t)(t % kRing) * TB, ln, qf, sc);
+        mask_tail16(sc, j0, kl.lane_lim, c2);
+        rescale_to<D>(tile_max16(sc, c2), m, l, acc);
+        ps = softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+      }
+      l += ps;
     } else {
-      valu_full();
+      valu_full(t);
     }
   };
   // Tiles between the first and the last: all full without a causal mask;
@@ -815,7 +890,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (CAUSAL)
       valu_any(t);
     else
-      valu_full();
+      valu_full(t);
   };
   auto pv_last = [&]() __attribute__((always_inline)) {
     uint32_t vq = ln.vq;
@@ -858,17 +933,17 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     block_barrier(); pv_last();  // slot 2T + 1
   }
 
-  const float lt = xhalf_sum(l);
-  const float inv = 1.0f / lt;
+  const float lt = xhalf_sum(l[0]);
+  const float inv = 1.0f / xhalf_sum(l[1]);
   const float lse = (m + log2f(lt)) * kLn2;
   if (sp.len) {
     if (qrow < N) store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv, lse);
   } else {
     static_assert(kPPThreads / 64 * 32 * 2 * D <= kRing * G::TILEB,
                   "the output staging must fit in the K ring");
-    // The K ring is free here: its last reader, the MFMA phase of the last
-    // tile, ended before this wave's last barrier, and every tile load has
-    // landed.  Wave w takes bytes
+    // The K ring is free here: its last reader, the VALU phase of the last
+    // tile (whose rare path may form S again from K), ended at this wave's
+    // last barrier, and every tile load has landed.  Wave w takes bytes
     // w * 32 * 2D .. of it (8 waves x 8 KiB = the 4 K slots at d = 128).
     store_rows_lds<E, D>((lds_u8*)smem + wave * 32 * 2 * D, Oh, LSE, L, bh, N,
                          qt * BM + wave * 32, acc, inv, lse);

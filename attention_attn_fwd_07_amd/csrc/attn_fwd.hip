@@ -389,6 +389,11 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   using G = Geo16<D, 4>;
   constexpr int BM = 128;
   static_assert(KS2 == 1 || (KS2 == 2 && !CAUSAL), "the key split is for the plain forward");
+  // Reference policy: with the key split at d = 64 (short rows, where the
+  // exact max would rescale on most tiles) the lagging reference and O
+  // divided by the rounded sum; otherwise the exact running max and O divided
+  // by l (at d = 128 the key split has no registers left for the second sum).
+  constexpr bool RSUM = KS2 == 2 && D == 64;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB * KS2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -438,7 +443,7 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   f32x16 acc[G::DB];
 #pragma unroll
   for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
-  f32x2 l = (f32x2){0.f, 0.f};  // row sum of the fp32 P ([1] unused here)
+  f32x2 l = (f32x2){0.f, 0.f};  // row sums of the fp32 P and (with RSUM) of the rounded P
 
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   block_barrier();
@@ -459,13 +464,13 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (j1 < Nk) loader.load_v(Vb, j1, Nk, vb_load);
     u32x4 pb[2][2];
     if (CAUSAL && kl.partial(J(t), G::BN))  // a diagonal tile (others are full)
-      l += softmax16<E, true, false>(cur, m, c2, pb, J(t), kl.lane_lim);
+      l += softmax16<E, true, RSUM>(cur, m, c2, pb, J(t), kl.lane_lim);
     else
-      l += softmax16<E, false, false>(cur, m, c2, pb, 0, 0);
+      l += softmax16<E, false, RSUM>(cur, m, c2, pb, 0, 0);
     qk16<E, D>(kb_next, qf, nxt);
     pv16<E, D>(vb_cur, pb, acc);
     if (kl.partial(j1, G::BN)) mask_tail16(nxt, j1, kl.lane_lim, c2);
-    maybe_rescale<D>(tile_max16(nxt, c2), m, l, acc, 0.f);
+    maybe_rescale<D>(tile_max16(nxt, c2), m, l, acc, RSUM ? kRescaleThreshold : 0.f);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads landed
     block_barrier();                                     // ... and everyone's
   };
@@ -476,9 +481,9 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // (a zero P times unloaded LDS could still make NaN), so nothing to add
     if (KS2 == 2 && j0 >= Nk) return;
     if (kl.partial(j0, G::BN))
-      l += softmax16<E, true, false>(cur, m, c2, pb, j0, kl.lane_lim);
+      l += softmax16<E, true, RSUM>(cur, m, c2, pb, j0, kl.lane_lim);
     else
-      l += softmax16<E, false, false>(cur, m, c2, pb, j0, 0);
+      l += softmax16<E, false, RSUM>(cur, m, c2, pb, j0, 0);
     pv16<E, D>(vb_cur, pb, acc);
   };
 
@@ -527,11 +532,10 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     m = mn;
   }
 
-  // Epilogue: O = acc / l (RNE to the element type), lse = (m + log2 l) ln 2.
-  // This kernel keeps the exact running max (threshold 0), so every P is at
-  // most 1 and a row's dominant key has P = 1 exactly: no rounded sum needed.
+  // Epilogue: O = acc / l (RNE to the element type; l[1], the rounded sum,
+  // with the lagging reference), lse = (m + log2 l[0]) ln 2.
   const float lt = xhalf_sum(l[0]);
-  const float inv = 1.0f / lt;
+  const float inv = 1.0f / (RSUM ? xhalf_sum(l[1]) : lt);
   const float lse = (m + log2f(lt)) * kLn2;
   if (sp.len) {
     if (qrow < N) store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv, lse);
@@ -693,11 +697,12 @@ struct PPLoader {
     koff = (uint32_t)(r0 * krs + ((p ^ swz_k<D>(r0)) << 4));
     voff = (uint32_t)(r0 * vrs + ((p ^ swz_v<D>(r0)) << 4));
   }
-  // Rows j0 .. j0+63 (j0 < N) of X (row stride rs bytes) into the tile at
-  // LDS byte address lds.
+  // Rows j0 .. j0+63 of X (row stride rs bytes) into the tile at LDS byte
+  // address lds.  A tile that starts at or past row N gets a descriptor of
+  // size 0: it reads as zeros and touches no memory.
   __device__ __forceinline__ void load(const unsigned char* Xb, uint32_t off, int rs, int j0,
                                        int N, uint32_t lds) const {
-    const i32x4 rsrc = buffer_rsrc(Xb + (size_t)j0 * rs, (N - j0) * rs);
+    const i32x4 rsrc = buffer_rsrc(Xb + (size_t)j0 * rs, j0 < N ? (N - j0) * rs : 0);
 #pragma unroll
     for (int u = 0; u < LPW; ++u)
       lds_dma16(rsrc, off + (uint32_t)(u * STEP_ROWS * rs),

@@ -158,6 +158,38 @@ __device__ __forceinline__ void store_rows_lds(lds_u8* area, uint16_t* __restric
   if (LSE != nullptr && hh == 0 && row0 + li < N) LSE[(size_t)bh * N + row0 + li] = lse;
 }
 
+// As store_rows_lds, for NB of the D/32 column blocks (H0 .. H0+NB-1) of the
+// wave's 32 rows: each row's NB * 64 bytes go through the wave's LDS area of
+// 32 x NB * 64 bytes and are stored as contiguous pieces of the row, 64 / (4 NB)
+// rows per instruction.  lse is written when LSE is not null.
+template <class E, int D, int H0, int NB>
+__device__ __forceinline__ void store_cols_lds(lds_u8* area, uint16_t* __restrict__ Oh,
+                                               float* __restrict__ LSE, const Layout& L, int bh,
+                                               int N, int row0, const f32x16 (&acc)[D / 32],
+                                               float inv, float lse) {
+  constexpr int ROWB = 64 * NB, CH = 4 * NB, RPI = 64 / CH;
+  const int lane = threadIdx.x & 63, li = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int h = 0; h < NB; ++h)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 4 * h + g;
+      const u32x2 w = (u32x2){E::pack2(acc[H0 + h][4 * g + 0] * inv, acc[H0 + h][4 * g + 1] * inv),
+                              E::pack2(acc[H0 + h][4 * g + 2] * inv, acc[H0 + h][4 * g + 3] * inv)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          area + li * ROWB + ((c ^ (li & (CH - 1))) << 4) + 8 * hh) = w;
+    }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CH, c = lane % CH;
+    const u32x4 x = *(const lds_u32x4*)(area + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
+    if (row0 + r < N)
+      *reinterpret_cast<u32x4*>(Oh + (size_t)(row0 + r) * L.o[2] + 32 * H0 + 8 * c) = x;
+  }
+  if (LSE != nullptr && hh == 0 && row0 + li < N) LSE[(size_t)bh * N + row0 + li] = lse;
+}
+
 // --- pieces of one K/V tile -------------------------------------------------
 
 // S^T = K Q^T for the two 32-key halves of a 64-key tile.  s[sb][r] is the
@@ -376,7 +408,8 @@ __device__ __forceinline__ void pv16(const lds_u8* vb, const u32x4 (&pb)[2][2],
 // take the same rows and alternate key tiles (even tiles to w, odd tiles to
 // w + 4), each with its own K/V buffers and online-softmax state; at the end
 // the two states are merged through LDS, m = max(m0, m1), acc and l scaled by
-// 2^(m_h - m).  This puts two waves on every SIMD when the grid alone gives
+// 2^(m_h - m), each half finalising and storing half of the output columns
+// of its rows.  This puts two waves on every SIMD when the grid alone gives
 // one.  Both halves run the same number of local tiles, so their barriers
 // pair up; with an odd tile count the odd half's last local tile lies past
 // the keys, is not loaded, and is fully masked.  Used without a causal mask
@@ -500,54 +533,80 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     last(t, sA, vbuf0);
   }
 
-  constexpr int NV = G::DB * 16 + 3;  // floats per lane in the key-split merge
-  if (KS2 == 2) {
-    // Merge the two halves' states through LDS (the K/V buffers are free once
-    // every wave is past its last PV product).  Half 1 writes its m, l and
-    // acc per lane; half 0 combines.  A half whose row saw no key has l = 0
-    // over the row and contributes nothing (its m may be -inf or NaN).
-    float* const xs = reinterpret_cast<float*>(smem) + (size_t)(rw * 64 + lane) * NV;
-    block_barrier();
-    if (kh == 1) {
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xs[db * 16 + r] = acc[db][r];
-      xs[G::DB * 16] = m;
-      xs[G::DB * 16 + 1] = l[0];
-      xs[G::DB * 16 + 2] = l[1];
-    }
-    block_barrier();
-    if (kh == 1) return;
-    const float m1 = xs[G::DB * 16];
-    const f32x2 l1 = (f32x2){xs[G::DB * 16 + 1], xs[G::DB * 16 + 2]};
-    const bool has1 = xhalf_sum(l1[0]) > 0.f;
-    const float mn = has1 ? fmaxf(m, m1) : m;
-    const float a0 = fast_exp2(m - mn), a1 = has1 ? fast_exp2(m1 - mn) : 0.f;
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * a0 + (has1 ? xs[db * 16 + r] * a1 : 0.f);
-    l = l * a0 + (has1 ? l1 * a1 : (f32x2){0.f, 0.f});
-    m = mn;
-  }
-
   // Epilogue: O = acc / l (RNE to the element type; l[1], the rounded sum,
   // with the lagging reference), lse = (m + log2 l[0]) ln 2.
-  const float lt = xhalf_sum(l[0]);
-  const float inv = 1.0f / (RSUM ? xhalf_sum(l[1]) : lt);
-  const float lse = (m + log2f(lt)) * kLn2;
-  if (sp.len) {
-    if (qrow < N) store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv, lse);
+  if constexpr (KS2 == 2) {
+    // Merge the two halves' states through LDS (the K/V buffers are free once
+    // every wave is past its last P V product).  Half kh finalises column
+    // blocks [kh HB, kh HB + HB) of its 32 rows: each wave hands its partner
+    // (same rows, other half) its m, l and the partner's column blocks, and
+    // both combine.  m = max of the two, each side scaled by 2^(m_side - m);
+    // the sums of products come out the same in both halves (the two terms
+    // commute), so the two halves agree on l and lse.  A half whose row saw
+    // no key has l = 0 over the row and contributes nothing (its m may be
+    // -inf); a NaN in either half's l reaches the output.
+    constexpr int HB = G::DB / 2;
+    constexpr int NX = 4 + 16 * HB;  // floats per lane: m, l[0], l[1], pad, the blocks
+    typedef __attribute__((address_space(3))) float lds_f32;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    lds_f32* const xbase = (lds_f32*)(lds_u8*)smem;
+    lds_f32* const mine = xbase + (rw * 2 + kh) * 64 * NX + lane * NX;
+    const lds_f32* const theirs = xbase + (rw * 2 + (kh ^ 1)) * 64 * NX + lane * NX;
+    auto give = [&](auto h0c) __attribute__((always_inline)) {
+      constexpr int H0 = decltype(h0c)::value;
+#pragma unroll
+      for (int h = 0; h < HB; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4)
+          *(lds_f32x4*)(mine + 4 + 16 * h + r) =
+              (f32x4){acc[H0 + h][r], acc[H0 + h][r + 1], acc[H0 + h][r + 2], acc[H0 + h][r + 3]};
+    };
+    block_barrier();
+    *(lds_f32x4*)mine = (f32x4){m, l[0], l[1], 0.f};
+    if (kh == 0) give(std::integral_constant<int, HB>{}); else give(std::integral_constant<int, 0>{});
+    block_barrier();
+    const f32x4 ml = *(const lds_f32x4*)theirs;
+    const f32x2 lo = (f32x2){ml[1], ml[2]};
+    const bool hs = xhalf_sum(l[0]) != 0.f, ho = xhalf_sum(lo[0]) != 0.f;  // NaN counts
+    const float mn = hs && ho ? fmaxf(m, ml[0]) : (hs ? m : ml[0]);
+    const float as = hs ? fast_exp2(m - mn) : 0.f, ao = ho ? fast_exp2(ml[0] - mn) : 0.f;
+    l = (hs ? l * as : (f32x2){0.f, 0.f}) + (ho ? lo * ao : (f32x2){0.f, 0.f});
+    m = mn;
+    const float lt = xhalf_sum(l[0]);
+    const float inv = 1.0f / (RSUM ? xhalf_sum(l[1]) : lt);
+    const float lse = (m + log2f(lt)) * kLn2;
+    // staging for this wave's 32 rows x HB blocks, past the exchange area
+    static_assert((8 * 64 * NX) * 4 + 8 * 32 * HB * 64 <= 4 * G::TILEB * KS2,
+                  "the merge and the output staging must fit");
+    lds_u8* const area = (lds_u8*)smem + (8 * 64 * NX) * 4 + (rw * 2 + kh) * 32 * HB * 64;
+    auto take = [&](auto h0c) __attribute__((always_inline)) {
+      constexpr int H0 = decltype(h0c)::value;
+#pragma unroll
+      for (int h = 0; h < HB; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const f32x4 x = *(const lds_f32x4*)(theirs + 4 + 16 * h + r);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            acc[H0 + h][r + u] = (hs ? acc[H0 + h][r + u] * as : 0.f) + (ho ? x[u] * ao : 0.f);
+        }
+      store_cols_lds<E, D, H0, HB>(area, Oh, kh == 0 ? LSE : nullptr, L, bh, N, qt * BM + rw * 32,
+                                   acc, inv, lse);
+    };
+    if (kh == 0) take(std::integral_constant<int, 0>{}); else take(std::integral_constant<int, HB>{});
   } else {
-    // Output staging: without the key split, the two K buffers (every wave
-    // read its last K tile before the last barrier it passed; only V is still
-    // read); with it, this wave's own part of the merge area, which only
-    // this wave has read since the merge's barrier.
-    static_assert(4 * 32 * 2 * D <= 2 * G::TILEB && 32 * 2 * D <= 64 * NV * 4,
-                  "the output staging must fit");
-    lds_u8* const area = KS2 == 2 ? (lds_u8*)smem + rw * 64 * NV * 4 : kbuf0 + rw * 32 * 2 * D;
-    store_rows_lds<E, D>(area, Oh, LSE, L, bh, N, qt * BM + rw * 32, acc, inv, lse);
+    const float lt = xhalf_sum(l[0]);
+    const float inv = 1.0f / (RSUM ? xhalf_sum(l[1]) : lt);
+    const float lse = (m + log2f(lt)) * kLn2;
+    if (sp.len) {
+      if (qrow < N) store_row16<E, D>(Oh, LSE, sp, L, bh, gridDim.x / nqt, N, qrow, acc, inv, lse);
+    } else {
+      // Output staging in the two K buffers (every wave read its last K tile
+      // before the last barrier it passed; only V is still read).
+      static_assert(4 * 32 * 2 * D <= 2 * G::TILEB, "the output staging must fit");
+      store_rows_lds<E, D>(kbuf0 + rw * 32 * 2 * D, Oh, LSE, L, bh, N, qt * BM + rw * 32, acc, inv,
+                           lse);
+    }
   }
 }
 

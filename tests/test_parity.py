@@ -301,9 +301,10 @@ def test_empty_sequence_is_a_no_op():
     assert o.shape == (2, 3, 0, 64) and lse.shape == (2, 3, 0)
 
 
-def test_nan_key_poisons_its_head_only():
+@pytest.mark.parametrize("key", [150, 100])  # the two key halves of the in-block split
+def test_nan_key_poisons_its_head_only(key):
     q, k, v = datagen.make_qkv(1, 2, 200, 64, "bf16", seed=12)
-    k[0, 0, 150, 3] = float("nan")
+    k[0, 0, key, 3] = float("nan")
     o, lse = run_gpu(q, k, v, 0.125)
     assert np.all(np.isnan(o[0, 0])) and np.all(np.isnan(lse[0, 0]))
     assert np.all(np.isfinite(o[0, 1])) and np.all(np.isfinite(lse[0, 1]))

@@ -1019,12 +1019,10 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 template <int D>
 struct Geo32 {
-  static constexpr int BM = 128;
   static constexpr int BN = 32;
   static constexpr int ROWB = D * 4;
   static constexpr int CH = D / 4;             // 16-byte chunks per row
   static constexpr int TILEB = BN * ROWB;
-  static constexpr int CPT = BN * CH / kThreads;
   static constexpr int QV = D / 2;             // Q values per lane
   static constexpr int DB = D / 32;
   static constexpr int SMEM = 4 * TILEB;
@@ -1039,15 +1037,28 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool CAUSAL>
+// KS > 1 (grids of a few blocks): the block's four waves split as RG = 4 / KS
+// row groups of 32 rows times KS key groups; key group kh takes the tiles
+// t = kh mod KS with its own double buffer, loaded by its own RG waves, and
+// at the end groups 1 .. KS-1 hand their (m, l, acc) to group 0 through LDS,
+// which merges them exactly as the per-tile rescale does.  Every group's
+// first tile holds keys (N >= 32 KS).  Without a causal mask.
+template <int D, bool CAUSAL, int KS = 1>
 __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c2, Layout L, Split sp) {
   using G = Geo32<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM];
+  static_assert(KS == 1 || !CAUSAL, "the key split is for the plain forward");
+  constexpr int RG = 4 / KS, BM = 32 * RG;
+  constexpr int GT = 64 * RG;                   // threads that load a key group's tiles
+  constexpr int CPT = G::BN * G::CH / GT;       // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::SMEM * KS];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hh = lane >> 5;
+  const int rw = wave % RG, kh = wave / RG;     // row group, key group
+  const int gt = rw * 64 + lane;                // thread index within the key group
+  unsigned char* const lsm = smem + kh * G::SMEM;
 
   const WorkItem wi = query_item<CAUSAL>(nqt);
   const int bh = wi.bh, qt = wi.t;
@@ -1060,8 +1071,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
 
   // Contraction index of K*Q^T: lane half hh covers d in [hh*D/2, (hh+1)*D/2),
   // one d per MFMA k-step.
-  const int qrow = qt * G::BM + wave * 32 + li;
-  const KeyLimit<CAUSAL> kl(Nk, qrow, qt * G::BM + wave * 32);
+  const int qrow = qt * BM + rw * 32 + li;
+  const KeyLimit<CAUSAL> kl(Nk, qrow, qt * BM + rw * 32);
   float qf[G::QV];
   if (qrow < N) {
     const f32x4* qp = reinterpret_cast<const f32x4*>(Qh + (size_t)qrow * L.q[2] + hh * G::QV);
@@ -1080,12 +1091,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   for (int db = 0; db < G::DB; ++db) acc[db] = (f32x16){};
   float m = -INFINITY, l = 0.f;
 
-  const int ntiles = key_tiles<CAUSAL>(Nk, qt * G::BM, G::BM, G::BN);
-  f32x4 kr[G::CPT], vr[G::CPT];
+  // local tile t of this key group is global tile KS t + kh; all groups run ntiles
+  const int ntiles = (key_tiles<CAUSAL>(Nk, qt * BM, BM, G::BN) + KS - 1) / KS;
+  f32x4 kr[CPT], vr[CPT];
   auto gload = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < G::CPT; ++u) {
-      const int ci = threadIdx.x + u * kThreads;
+    for (int u = 0; u < CPT; ++u) {
+      const int ci = gt + u * GT;
       const int row = ci / G::CH, c = ci % G::CH;
       if (j0 + row < Nk) {
         kr[u] = *reinterpret_cast<const f32x4*>(Kh + (size_t)(j0 + row) * L.k[2] + c * 4);
@@ -1098,22 +1110,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   };
   auto swrite = [&](unsigned char* kb, unsigned char* vb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < G::CPT; ++u) {
-      const int ci = threadIdx.x + u * kThreads;
+    for (int u = 0; u < CPT; ++u) {
+      const int ci = gt + u * GT;
       const int row = ci / G::CH, c = ci % G::CH;
       *reinterpret_cast<f32x4*>(kb + row * G::ROWB + ((c ^ swz32_k<D>(row)) << 4)) = kr[u];
       *reinterpret_cast<f32x4*>(vb + row * G::ROWB + ((c ^ swz32_v<D>(row)) << 4)) = vr[u];
     }
   };
-  gload(0);
-  swrite(smem, smem + G::TILEB);
+  gload(kh * G::BN);
+  swrite(lsm, lsm + G::TILEB);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * G::BN;
+    const int j0 = (KS * t + kh) * G::BN;
     const bool more = t + 1 < ntiles;
-    if (more) gload(j0 + G::BN);
-    const unsigned char* kb = smem + (t & 1) * 2 * G::TILEB;
+    if (more) gload(j0 + KS * G::BN);
+    const unsigned char* kb = lsm + (t & 1) * 2 * G::TILEB;
     const unsigned char* vb = kb + G::TILEB;
 
     // S^T = K Q^T for 32 keys.
@@ -1170,10 +1182,59 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
       }
     }
     if (more) {
-      unsigned char* nb = smem + ((t + 1) & 1) * 2 * G::TILEB;
+      unsigned char* nb = lsm + ((t + 1) & 1) * 2 * G::TILEB;
       swrite(nb, nb + G::TILEB);
     }
     __syncthreads();
+  }
+
+  if constexpr (KS > 1) {
+    // groups 1 .. KS-1 write (acc, m, l) per lane; group 0 merges.  A group
+    // whose row saw no key has l = 0 and adds nothing; a NaN l is kept.
+    constexpr int NV = G::DB * 16 + 2;
+    static_assert((KS - 1) * RG * 64 * NV * 4 <= G::SMEM * KS, "the merge area must fit");
+    float* const xs = reinterpret_cast<float*>(smem);
+    auto slot = [&](int g) __attribute__((always_inline)) {
+      return xs + (size_t)(((g - 1) * RG + rw) * 64 + lane) * NV;
+    };
+    if (kh > 0) {
+      float* const x = slot(kh);
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[db * 16 + r] = acc[db][r];
+      x[G::DB * 16] = m;
+      x[G::DB * 16 + 1] = l;
+    }
+    __syncthreads();
+    if (kh > 0) return;
+    float mg[KS], lg[KS];
+    bool hg[KS];
+    mg[0] = m, lg[0] = l, hg[0] = xhalf_sum(l) != 0.f;
+    float mn = hg[0] ? m : -INFINITY;
+#pragma unroll
+    for (int g = 1; g < KS; ++g) {
+      mg[g] = slot(g)[G::DB * 16];
+      lg[g] = slot(g)[G::DB * 16 + 1];
+      hg[g] = xhalf_sum(lg[g]) != 0.f;
+      if (hg[g]) mn = fmaxf(mn, mg[g]);
+    }
+    const float a0 = hg[0] ? fast_exp2(m - mn) : 0.f;
+    l = hg[0] ? l * a0 : 0.f;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) acc[db] = hg[0] ? acc[db] * a0 : (f32x16){};
+#pragma unroll
+    for (int g = 1; g < KS; ++g) {
+      if (!hg[g]) continue;
+      const float ag = fast_exp2(mg[g] - mn);
+      const float* const x = slot(g);
+      l += lg[g] * ag;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] += x[db * 16 + r] * ag;
+    }
+    m = mn;
   }
 
   const float lt = xhalf_sum(l);
@@ -1345,6 +1406,19 @@ int launch16(const Launch& a) {
 template <bool C>
 int launch32(const Launch& a) {
   const int64_t nqt = (a.N + 127) / 128;
+  // Few blocks (at most a quarter of the CUs): split each block's keys over
+  // its waves (4 groups of 32-key tiles at d = 64, 2 at d = 128, where the
+  // LDS holds two groups' buffers) and use more, shorter blocks.
+  if (!C && a.splits == 1 && a.bh * nqt * a.splits <= kNumCUs / 4) {
+    if (a.d == 64 && a.N >= 4 * 32) {
+      const int64_t n = (a.N + 31) / 32;
+      return launch<float>(attn_fwd_mfma32<64, false, 4>, a.bh * n, kThreads, (int)n, a);
+    }
+    if (a.d == 128 && a.N >= 2 * 32) {
+      const int64_t n = (a.N + 63) / 64;
+      return launch<float>(attn_fwd_mfma32<128, false, 2>, a.bh * n, kThreads, (int)n, a);
+    }
+  }
   auto kern = a.d == 128 ? attn_fwd_mfma32<128, C> : attn_fwd_mfma32<64, C>;
   return launch<float>(kern, a.bh * nqt, kThreads, (int)nqt, a);
 }

@@ -301,9 +301,14 @@ def test_empty_sequence_is_a_no_op():
     assert o.shape == (2, 3, 0, 64) and lse.shape == (2, 3, 0)
 
 
-@pytest.mark.parametrize("key", [150, 100])  # the two key halves of the in-block split
-def test_nan_key_poisons_its_head_only(key):
-    q, k, v = datagen.make_qkv(1, 2, 200, 64, "bf16", seed=12)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("key", [150, 100])
+def test_nan_key_poisons_its_head_only(dtype, key):
+    """A NaN in one key row of head 0 makes every output row of that head NaN
+    and leaves head 1 finite.  N = 200 runs the in-block key splits: key 150
+    is in the first key group of either split (64-key tiles over two halves
+    at bf16, 32-key tiles over four groups at fp32), key 100 in another."""
+    q, k, v = datagen.make_qkv(1, 2, 200, 64, dtype, seed=12)
     k[0, 0, key, 3] = float("nan")
     o, lse = run_gpu(q, k, v, 0.125)
     assert np.all(np.isnan(o[0, 0])) and np.all(np.isnan(lse[0, 0]))

@@ -12,6 +12,7 @@ GPU is present, calls raise.
     o, lse = fwd_splitkv(q, k, v, splits=8)  # keys split over 8 blocks, then merged
     attn_fwd_splitkv_static(q, k, v, o, lse, scale, 4)  # no workspace, no allocation
     dq, dk, dv = bwd(q, k, v, o, lse, do)    # gradients (include/attn_bwd.h)
+    o = attention(q, k, v)                 # with autograd: o.backward(do) runs attn_bwd
 
 Tensors are ``[B, H, N, d]`` fp32/fp16/bf16 with d in {64, 128}; the head
 dimension must be contiguous, the other three dimensions may have any strides
@@ -32,7 +33,8 @@ from .build import LIB
 
 __all__ = ["attn_fwd", "fwd", "plan", "Plan", "attn_strerror", "attn_version", "library_path",
            "AttnError", "ATTN_CAUSAL", "splitkv_workspace_size", "fwd_splitkv", "attn_bwd",
-           "bwd", "bwd_workspace_size", "attn_fwd_splitkv_static", "STATIC_WORKSPACE_BYTES"]
+           "bwd", "bwd_workspace_size", "attn_fwd_splitkv_static", "STATIC_WORKSPACE_BYTES",
+           "attention"]
 
 STATIC_WORKSPACE_BYTES = 64 << 20  # ATTN_STATIC_WORKSPACE_BYTES of include/attn_fwd.h
 
@@ -393,3 +395,42 @@ def bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False)
     ws = torch.empty(max(4, nbytes) // 4, dtype=torch.float32, device=q.device)
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, ws, causal=causal)
     return dq, dk, dv
+
+
+_ATTENTION_FN = None
+
+
+def _attention_fn():
+    """The autograd Function behind ``attention`` (made on first use, since
+    torch is imported lazily)."""
+    global _ATTENTION_FN
+    if _ATTENTION_FN is None:
+        torch = _torch()
+
+        class AttentionFn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, scale, causal):
+                o, lse = fwd(q, k, v, scale, True, causal)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.scale, ctx.causal = scale, causal
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), ctx.scale, ctx.causal)
+                return dq, dk, dv, None, None
+
+        _ATTENTION_FN = AttentionFn
+    return _ATTENTION_FN
+
+
+def attention(q, k, v, scale: float | None = None, causal: bool = False):
+    """O = softmax(scale Q K^T) V as a differentiable torch op: the forward runs
+    ``attn_fwd`` and keeps q, k, v, O and the log-sum-exp; the backward runs
+    ``attn_bwd`` on them (page 3 "OpenAI Triton from introduction to model
+    practice", section 6: the autograd wrapper saves q, k, v, o and lse for the
+    backward).  Gradients need bf16/fp16 and contiguous q, k, v."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _attention_fn().apply(q, k, v, float(scale), bool(causal))

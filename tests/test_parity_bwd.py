@@ -168,3 +168,26 @@ def test_bwd_binding_rejects_fp32_and_missing_lse():
     qb = q.bfloat16()
     with pytest.raises(ValueError):
         attn.bwd(qb, qb, qb, qb, None, qb)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_wrapper(causal):
+    """attention() as a torch op: O equals fwd's, the gradients equal the
+    direct attn_bwd call's (the same kernels on the same saved tensors), and
+    those hold the oracle's bounds."""
+    attn = _attn()
+    q, k, v = datagen.make_qkv(1, 2, 300, 64, "bf16", seed=811)
+    g = datagen.make_qkv(1, 2, 300, 64, "bf16", seed=812)[0]
+    scale = 0.125
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev).requires_grad_(True) for t in (q, k, v))
+    o = attn.attention(qd, kd, vd, scale, causal=causal)
+    o.backward(g.to(dev))
+    o_ref, lse_ref = attn.fwd(qd.detach(), kd.detach(), vd.detach(), scale, causal=causal)
+    grads = attn.bwd(qd.detach(), kd.detach(), vd.detach(), o_ref, lse_ref, g.to(dev), scale,
+                     causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref)
+    for got, want in zip((qd.grad, kd.grad, vd.grad), grads):
+        assert torch.equal(got, want)
+    check_grads(q, k, v, g, scale, causal, "bf16", f"autograd causal={causal}")

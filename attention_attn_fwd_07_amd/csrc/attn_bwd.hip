@@ -10,11 +10,11 @@
 // Like the forward, nothing of size N x N reaches device memory: each block
 // recomputes its tiles of s and P from Q, K and the stored lse.
 //
-// Three kernels:
-//   * delta:  per query row the pair (lse log2 e, D = rowsum(dO * O)), into
-//             the workspace;
-//   * dq:     one block = 128 query rows (4 waves); it loops over key tiles
-//             and accumulates dQ^T = K^T dS^T in registers (the forward's
+// Two kernels:
+//   * dq:     one block = 128 query rows (4 waves); it first forms per query
+//             row the pair (lse log2 e, D = rowsum(dO * O)) and stores it in
+//             the workspace for dkdv, then loops over key tiles and
+//             accumulates dQ^T = K^T dS^T in registers (the forward's
 //             layout: lane l owns query row l % 32 of its wave);
 //   * dkdv:   one block = 256 keys (8 waves); it loops over query tiles and
 //             accumulates dK^T = Q^T dS and dV^T = dO^T P (the transposed
@@ -179,29 +179,6 @@ struct Widen<F16T> {
   }
 };
 
-// Per query row: (lse * log2 e, D = rowsum(dO * O)), the two statistics both
-// gradient kernels read, as one 8-byte pair (so that one load brings both).
-template <class E, int D>
-__global__ __launch_bounds__(256) void attn_bwd_delta(const uint16_t* __restrict__ O,
-                                                      const uint16_t* __restrict__ dO,
-                                                      const float* __restrict__ LSE,
-                                                      float2* __restrict__ stats, long long rows) {
-  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const u32x4* po = reinterpret_cast<const u32x4*>(O + (size_t)r * D);
-  const u32x4* pd = reinterpret_cast<const u32x4*>(dO + (size_t)r * D);
-  float acc = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < D / 8; ++c) {
-    float a[8], b[8];
-    Widen<E>::get(po[c], a);
-    Widen<E>::get(pd[c], b);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf(a[i], b[i], acc);
-  }
-  stats[r] = make_float2(LSE[r] * kLog2e, acc);
-}
-
 // Loads of ROWS rows of a [N, D] tensor (rows 2D bytes apart in memory) into
 // a dense LDS tile in the swz_b layout, by NW waves: 16-byte direct
 // global->LDS loads, one buffer descriptor per tile whose range ends at row
@@ -243,7 +220,8 @@ template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                 const float2* __restrict__ stats, uint16_t* __restrict__ dQ, int N, int nqt,
+                 const uint16_t* __restrict__ O, const float* __restrict__ LSE,
+                 float2* __restrict__ stats, uint16_t* __restrict__ dQ, int N, int nqt,
                  float c2, float scale) {
   using G = Geo16<D, 4>;
   constexpr int TB = G::TILEB, KS = D / 16, DB = D / 32;
@@ -270,16 +248,30 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   load(0, 0);
 
   const int qrow = q0 + wave * 32 + li;
-  u32x4 qf[KS], df[KS];
+  u32x4 qf[KS], df[KS], of[KS];
   load_row_frag<D>(Q + hoff, qrow, N, qf);
   load_row_frag<D>(dO + hoff, qrow, N, df);
-  const float2 st = qrow < N ? stats[(size_t)bh * N + qrow] : make_float2(INFINITY, 0.f);
-  const float lse2 = st.x, dl = st.y;
+  load_row_frag<D>(O + hoff, qrow, N, of);
+  const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
   const int lim = CAUSAL ? min(N - 1, qrow) : N - 1;         // last key this row sees
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
   wait_vmcnt<0>();
+  // D = rowsum(dO * O) of the row, from the two lane halves' d ranges (rows
+  // past N have zero fragments, D = 0); stored with lse log2 e for the dK/dV
+  // kernel, which runs after this one.
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float a[8], b[8];
+    Widen<E>::get(of[ks], a);
+    Widen<E>::get(df[ks], b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dpart = fmaf(a[i], b[i], dpart);
+  }
+  const float dl = xhalf_sum(dpart);
+  if (hh == 0 && qrow < N) stats[(size_t)bh * N + qrow] = make_float2(lse2, dl);
   // The compiler cannot see the DMA loads (inline asm); using the row
   // fragments here retires their loads in its bookkeeping, so that it places
   // no wait of its own inside the loop, where tile loads are in flight.
@@ -586,18 +578,14 @@ bool overlap_b(const void* a, size_t na, const void* b, size_t nb) {
 template <class E, int D, bool C>
 int launch_bwd(const attn_bwd_args_t& a, float2* stats, int64_t bh) {
   hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
-  const int64_t rows = bh * a.N;
   const float c2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_bwd_delta<E, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                     s, static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                     a.lse, stats, (long long)rows);
-  if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   const int64_t nt = (a.N + kBM - 1) / kBM;
   const uint16_t *q = static_cast<const uint16_t*>(a.q), *k = static_cast<const uint16_t*>(a.k),
                  *v = static_cast<const uint16_t*>(a.v),
                  *dout = static_cast<const uint16_t*>(a.dout);
   hipLaunchKernelGGL((attn_bwd_dq<E, D, C>), dim3((unsigned)(bh * nt)), dim3(256), 0, s, q, k, v,
-                     dout, stats, static_cast<uint16_t*>(a.dq), (int)a.N, (int)nt, c2, a.scale);
+                     dout, static_cast<const uint16_t*>(a.o), a.lse, stats,
+                     static_cast<uint16_t*>(a.dq), (int)a.N, (int)nt, c2, a.scale);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   const int64_t nkt = (a.N + kBK - 1) / kBK;
   hipLaunchKernelGGL((attn_bwd_dkdv<E, D, C>), dim3((unsigned)(bh * nkt)), dim3(64 * kKW), 0, s,

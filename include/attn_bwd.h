@@ -68,10 +68,10 @@ typedef struct attn_bwd_args {
 size_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d);
 
 /*
- * attn_bwd - dQ, dK, dV (see above).  Three kernels queued on args->stream:
- * the per-row (lse * log2(e), D) pairs into the workspace, then dQ (blocks
- * over query rows) and dK, dV (blocks over keys), with no atomics
- * (deterministic).
+ * attn_bwd - dQ, dK, dV (see above).  Two kernels queued on args->stream:
+ * dQ (blocks over query rows; each block first stores its rows'
+ * (lse * log2(e), D) pairs in the workspace), then dK, dV (blocks over keys,
+ * reading those pairs), with no atomics (deterministic).
  *
  * workspace : device memory, 16-byte aligned, at least attn_bwd_workspace()
  *             bytes, not overlapping any tensor; owned by the caller.

@@ -414,9 +414,10 @@ __device__ __forceinline__ void pv16(const lds_u8* vb, const u32x4 (&pb)[2][2],
 // pair up; with an odd tile count the odd half's last local tile lies past
 // the keys, is not loaded, and is fully masked.  Used without a causal mask
 // or a split, for at least two key tiles.
-// Occupancy: at d = 64 without the key split the kernel fits in 168 VGPRs,
-// so three blocks share a CU (three waves per SIMD; measured 2 % faster than
-// two at N = 65536); otherwise two.
+// Register budget: at d = 64 without the key split the kernel is compiled for
+// three waves per SIMD (at most 168 VGPRs; three blocks of four waves share a
+// CU), which measured 2 % faster at N = 65536 than the build for two;
+// otherwise for two waves per SIMD (up to 256 VGPRs).
 template <class E, int D, bool CAUSAL, int KS2>
 __global__ __launch_bounds__(kThreads * KS2)
 __attribute__((amdgpu_waves_per_eu(D == 64 && KS2 == 1 ? 3 : 2)))

@@ -17,7 +17,9 @@
 //                     software-pipelined in each wave; for grids of at most
 //                     one block per CU, 8 waves with the keys split between
 //                     two waves per row group;
-//   * attn_fwd_mfma32 fp32: the same structure on the fp32 MFMA;
+//   * attn_fwd_mfma32 fp32: the same structure on the fp32 MFMA; for grids of
+//                     a few blocks, shorter blocks whose four waves split
+//                     the keys (four key groups at d = 64, two at d = 128);
 //   * attn_merge      the split-KV merge.
 // All take a causal flag, element strides and a key-range split.
 //
@@ -276,11 +278,12 @@ __device__ __forceinline__ float tile_max16(const f32x16 (&s)[2], float c2) {
 // threshold, therefore normalises O by the sum of the same rounded P (l[1]
 // below), so the weights applied to V sum to one exactly and that rounding
 // cancels between numerator and denominator, while the log-sum-exp uses the
-// sum of the unrounded P (l[0]).  The pipelined kernel instead follows the
-// exact running max (threshold 0: every P is at most 1 and the key that sets
-// a row's max has P = 1 exactly) and normalises by l[0]; at d = 64 its VALU
-// work sets its speed, and the rare extra rescales of long rows cost less
-// than the rounded sum would.
+// sum of the unrounded P (l[0]).  The pipelined kernel with its in-block key
+// split at d = 64 (short rows) does the same.  Otherwise the pipelined kernel
+// follows the exact running max (threshold 0: every P is at most 1 and the
+// key that sets a row's max has P = 1 exactly) and normalises by l[0]; at
+// d = 64 its VALU work sets its speed, and on long rows the rare extra
+// rescales cost less than the rounded sum would.
 constexpr float kRescaleThreshold = 8.0f;
 
 // Move each row's reference to max(m, m_tile) and rescale its l and

@@ -191,3 +191,25 @@ def test_autograd_wrapper(causal):
     for got, want in zip((qd.grad, kd.grad, vd.grad), grads):
         assert torch.equal(got, want)
     check_grads(q, k, v, g, scale, causal, "bf16", f"autograd causal={causal}")
+
+
+def _bwd_case(i):
+    rng = np.random.default_rng(9100 + i)
+    dtype = ["bf16", "f16"][int(rng.integers(2))]
+    d = [64, 128][int(rng.integers(2))]
+    N = int(np.exp(rng.uniform(0.0, math.log(1200.0))))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    causal = bool(rng.integers(2))
+    scale = 1.0 / math.sqrt(d) if rng.random() < 0.6 else float(rng.uniform(-0.3, 0.4))
+    return dtype, d, N, B, H, causal, scale, 9100 + i
+
+
+@pytest.mark.parametrize("i", range(24), ids=lambda i: "{}-{}-d{}-N{}-B{}H{}-{}".format(
+    i, *_bwd_case(i)[:5], "causal" if _bwd_case(i)[5] else "plain"))
+def test_bwd_random_case(i):
+    """A seeded random sweep (dtype, head dim, N, B, H, causal, scale): every
+    gradient element within its derived bound, rel-F within 2u."""
+    dtype, d, N, B, H, causal, scale, seed = _bwd_case(i)
+    q, k, v = datagen.make_qkv(B, H, N, d, dtype, seed=seed)
+    g = datagen.make_qkv(B, H, N, d, dtype, seed=seed + 50000)[0]
+    check_grads(q, k, v, g, scale, causal, dtype, f"random bwd case {i}")

@@ -14,12 +14,13 @@ GPU is present, calls raise.
     dq, dk, dv = bwd(q, k, v, o, lse, do)    # gradients (include/attn_bwd.h)
     o = attention(q, k, v)                 # with autograd: o.backward(do) runs attn_bwd
 
-Tensors are ``[B, H, N, d]`` fp32/fp16/bf16 with d in {64, 128}; the head
-dimension must be contiguous, the other three dimensions may have any strides
-that are multiples of 8 elements (so a ``[B, N, H, d]`` tensor viewed with
-``.transpose(1, 2)`` is accepted without a copy).  ``lse`` is ``[B, H, N]``
-fp32 contiguous (or None).  ``causal=True`` restricts query row i to keys
-0..i.  Argument errors raise ValueError, mirroring a wrapper that checks
+Tensors are ``[B, H, N, d]`` fp32/fp16/bf16 with d in {64, 128}; k and v may
+have their own number of rows Nk (``[B, H, Nk, d]``: a few queries against a
+long key/value history), q, o and lse keep N.  The head dimension must be
+contiguous, the other three dimensions may have any strides that are multiples
+of 8 elements (so a ``[B, N, H, d]`` tensor viewed with ``.transpose(1, 2)`` is
+accepted without a copy).  ``lse`` is ``[B, H, N]`` fp32 contiguous (or None).
+``causal=True`` (only with Nk = N) restricts query row i to keys 0..i.  Argument errors raise ValueError, mirroring a wrapper that checks
 device, shape, dtype and layout before it launches anything (page 2 "Triton
 programming template", Python wrapper).
 """
@@ -64,7 +65,7 @@ class _Args(ctypes.Structure):
                 ("flags", ctypes.c_uint),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
                 ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
-                ("stream", ctypes.c_void_p)]
+                ("stream", ctypes.c_void_p), ("Nk", ctypes.c_int64)]
 
 
 class AttnError(ValueError):
@@ -103,6 +104,8 @@ def _load():
     lib.attn_fwd_splitkv_static.restype = ctypes.c_int
     lib.attn_fwd_splitkv_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.attn_fwd_splitkv_workspace.restype = ctypes.c_size_t
+    lib.attn_fwd_splitkv_workspace_ex.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.attn_fwd_splitkv_workspace_ex.restype = ctypes.c_size_t
     lib.attn_bwd.argtypes = [ctypes.POINTER(_BwdArgs), vp, ctypes.c_size_t]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_workspace.argtypes = [i64, i64, i64, i64]
@@ -145,9 +148,13 @@ def _check(q, k, v, o, lse):
             raise ValueError(f"{name} must be 4-D [B, H, N, d]")
         if t.numel() > 0 and t.stride(3) != 1 and t.shape[3] > 1:
             raise ValueError(f"{name}: the head dimension must be contiguous")
-    if not (q.shape == k.shape == v.shape == o.shape):
+    # q and o: [B, H, N, d]; k and v: [B, H, Nk, d] with Nk >= 1 keys when N > 0
+    if not (q.shape == o.shape and k.shape == v.shape and q.shape[:2] == k.shape[:2]
+            and q.shape[3] == k.shape[3]):
         raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} "
                          f"v{tuple(v.shape)} o{tuple(o.shape)}")
+    if k.shape[2] == 0 and q.numel() > 0:
+        raise ValueError("k and v have no rows: a softmax over no keys is undefined")
     if not (q.dtype == k.dtype == v.dtype == o.dtype):
         raise ValueError("q, k, v and o must share one dtype")
     if q.dtype not in codes:
@@ -225,6 +232,7 @@ class Plan:
         a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
         a.lse = lse.data_ptr() if lse is not None else None
         a.B, a.H, a.N, a.d = B, H, N, d
+        a.Nk = int(k.shape[2])
         a.scale = float(scale)
         a.dtype = code_dtype
         a.flags = ATTN_CAUSAL if causal else 0
@@ -268,9 +276,13 @@ def plan(q, k, v, o, lse, scale: float, stream=None, causal: bool = False, split
     return Plan(q, k, v, o, lse, scale, stream, causal, splits, workspace)
 
 
-def splitkv_workspace_size(B: int, H: int, N: int, d: int, splits: int) -> int:
-    """Bytes of workspace ``attn_fwd_splitkv`` needs (0 for empty sizes)."""
-    return int(_load().attn_fwd_splitkv_workspace(B, H, N, d, splits))
+def splitkv_workspace_size(B: int, H: int, N: int, d: int, splits: int,
+                           Nk: int | None = None) -> int:
+    """Bytes of workspace ``attn_fwd_splitkv`` needs for N query rows and Nk
+    key rows per head (Nk defaults to N; 0 for empty sizes)."""
+    if Nk is None:
+        return int(_load().attn_fwd_splitkv_workspace(B, H, N, d, splits))
+    return int(_load().attn_fwd_splitkv_workspace_ex(B, H, N, Nk, d, splits))
 
 
 def fwd_splitkv(q, k, v, scale: float | None = None, splits: int = 4, workspace=None,
@@ -286,7 +298,7 @@ def fwd_splitkv(q, k, v, scale: float | None = None, splits: int = 4, workspace=
     lse = (torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
            if return_lse else None)
     if workspace is None:
-        nbytes = splitkv_workspace_size(B, H, N, d, splits)
+        nbytes = splitkv_workspace_size(B, H, N, d, splits, int(k.shape[2]))
         workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=q.device)
     p = Plan(q, k, v, o, lse, scale, None, False, splits, workspace)
     if torch.cuda.current_device() == p.device.index:
@@ -352,6 +364,8 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, workspace, stream=
     and ``lse`` and the upstream gradient ``dout``.  Asynchronous on ``stream``."""
     torch = _torch()
     code = _check(q, k, v, o, lse)
+    if k.shape != q.shape:
+        raise ValueError("the backward is for self-attention: k and v need q's shape")
     for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         if not isinstance(t, torch.Tensor) or t.device != q.device:
             raise ValueError(f"{name} must be a tensor on q's device")

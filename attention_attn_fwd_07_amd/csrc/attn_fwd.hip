@@ -72,17 +72,20 @@ struct Layout {
   }
 };
 
-// Key split of the split-KV path.  With len > 0, block (x, y) of the grid
-// covers key rows y*len .. min(N, (y+1)*len) - 1 only and writes its own
-// normalised output and log-sum-exp, in fp32, to opart[y][b*H+h][row][d] and
+// The keys of a head and their split over blocks.  nk is the number of key
+// (and value) rows per head, which need not equal the number of query rows.
+// With len > 0 (the split-KV path), block (x, y) of the grid covers key rows
+// y*len .. min(nk, (y+1)*len) - 1 only and writes its own normalised output
+// and log-sum-exp, in fp32, to opart[y][b*H+h][row][d] and
 // lpart[y][b*H+h][row]; a second kernel merges the splits.  len == 0: one
 // block covers all keys and writes the final O and lse.
 struct Split {
   int len;
+  int nk;
   float* opart;
   float* lpart;
   __device__ __forceinline__ int first_key() const { return len ? (int)blockIdx.y * len : 0; }
-  __device__ __forceinline__ int keys(int N) const { return len ? min(N - first_key(), len) : N; }
+  __device__ __forceinline__ int keys() const { return len ? min(nk - first_key(), len) : nk; }
 };
 
 // Stores of one query row's result (the lane's 16 columns of each 32-column
@@ -451,7 +454,7 @@ void attn_fwd_mfma16(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const uint16_t* const Qh = Q + L.base(L.q, bh);
   uint16_t* const Oh = O + L.base(L.o, bh);
   // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
-  const int kb0 = sp.first_key(), Nk = sp.keys(N);
+  const int kb0 = sp.first_key(), Nk = sp.keys();
   const unsigned char* Kb =
       reinterpret_cast<const unsigned char*>(K + L.base(L.k, bh) + (long long)kb0 * L.k[2]);
   const unsigned char* Vb =
@@ -834,7 +837,7 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const uint16_t* const Qh = Q + L.base(L.q, bh);
   uint16_t* const Oh = O + L.base(L.o, bh);
   // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
-  const int kb0 = sp.first_key(), Nk = sp.keys(N);
+  const int kb0 = sp.first_key(), Nk = sp.keys();
   const unsigned char* Kb =
       reinterpret_cast<const unsigned char*>(K + L.base(L.k, bh) + (long long)kb0 * L.k[2]);
   const unsigned char* Vb =
@@ -1050,7 +1053,8 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
 // t = kh mod KS with its own double buffer, loaded by its own RG waves, and
 // at the end groups 1 .. KS-1 hand their (m, l, acc) to group 0 through LDS,
 // which merges them exactly as the per-tile rescale does.  Every group's
-// first tile holds keys (N >= 32 KS).  Without a causal mask.
+// first tile holds keys (at least 32 KS keys per head).  Without a causal
+// mask.
 template <int D, bool CAUSAL, int KS = 1>
 __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -1072,7 +1076,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
   const int bh = wi.bh, qt = wi.t;
   const float* Qh = Q + L.base(L.q, bh);
   // this block's keys: rows kb0 .. kb0 + Nk - 1 of the head (all of them without a split)
-  const int kb0 = sp.first_key(), Nk = sp.keys(N);
+  const int kb0 = sp.first_key(), Nk = sp.keys();
   const float* Kh = K + L.base(L.k, bh) + (long long)kb0 * L.k[2];
   const float* Vh = V + L.base(L.v, bh) + (long long)kb0 * L.v[2];
   float* const Oh = O + L.base(L.o, bh);
@@ -1347,7 +1351,7 @@ struct Launch {
   const void *q, *k, *v;
   void* o;
   float* lse;
-  int64_t bh, N, d;
+  int64_t bh, N, nk, d;  // heads, query rows, key rows, head dimension
   float c2;
   Layout L;
   Split sp;    // sp.len == 0: no split
@@ -1384,11 +1388,14 @@ bool use_pingpong(int64_t blocks256, int64_t d) {
 }
 
 // The pipelined kernel's in-block key split: when the grid of 128-row blocks
-// gives at most one block per CU (one wave per SIMD), without a causal mask
-// or a split and with at least two key tiles.  ATTN_FWD_KERNEL=pipelined
-// turns it off, =pipelined2 forces it where it applies (tests and sweeps).
-bool use_key_split(int64_t blocks128, int64_t N, bool causal, int splits) {
-  if (causal || splits != 1 || N <= 64) return false;
+// gives at most one block per CU (one wave per SIMD), without a causal mask,
+// outside the split-KV path (its epilogue writes the final O only, not the
+// fp32 partial results a split-KV call merges, even when that call ends up
+// with a single split) and with at least two key tiles (nk > 64).
+// ATTN_FWD_KERNEL=pipelined turns it off, =pipelined2 forces it where it
+// applies (tests and sweeps).
+bool use_key_split(int64_t blocks128, int64_t nk, bool causal, bool splitkv) {
+  if (causal || splitkv || nk <= 64) return false;
   const char* env = getenv("ATTN_FWD_KERNEL");
   if (env != nullptr && strcmp(env, "pipelined2") == 0) return true;
   if (env != nullptr && strcmp(env, "pipelined") == 0) return false;
@@ -1403,7 +1410,7 @@ int launch16(const Launch& a) {
     return launch<T>(kern, a.bh * nqt, kPPThreads, (int)nqt, a);
   }
   const int64_t nqt = (a.N + 127) / 128;
-  if (use_key_split(a.bh * nqt, a.N, C, a.splits)) {
+  if (use_key_split(a.bh * nqt, a.nk, C, a.sp.len != 0)) {
     auto kern = a.d == 128 ? attn_fwd_mfma16<E, 128, false, 2> : attn_fwd_mfma16<E, 64, false, 2>;
     return launch<T>(kern, a.bh * nqt, 2 * kThreads, (int)nqt, a);
   }
@@ -1416,13 +1423,15 @@ int launch32(const Launch& a) {
   const int64_t nqt = (a.N + 127) / 128;
   // Few blocks (at most a quarter of the CUs): split each block's keys over
   // its waves (4 groups of 32-key tiles at d = 64, 2 at d = 128, where the
-  // LDS holds two groups' buffers) and use more, shorter blocks.
-  if (!C && a.splits == 1 && a.bh * nqt * a.splits <= kNumCUs / 4) {
-    if (a.d == 64 && a.N >= 4 * 32) {
+  // LDS holds two groups' buffers) and use more, shorter blocks.  Every
+  // group's first tile must hold keys (nk >= 32 groups); not on the split-KV
+  // path, whose blocks may hold a single key.
+  if (!C && a.sp.len == 0 && a.bh * nqt <= kNumCUs / 4) {
+    if (a.d == 64 && a.nk >= 4 * 32) {
       const int64_t n = (a.N + 31) / 32;
       return launch<float>(attn_fwd_mfma32<64, false, 4>, a.bh * n, kThreads, (int)n, a);
     }
-    if (a.d == 128 && a.N >= 2 * 32) {
+    if (a.d == 128 && a.nk >= 2 * 32) {
       const int64_t n = (a.N + 63) / 64;
       return launch<float>(attn_fwd_mfma32<128, false, 2>, a.bh * n, kThreads, (int)n, a);
     }
@@ -1526,7 +1535,8 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
             bool static_ws = false) {
   // --- validation: no HIP call before this block has passed -------------
   const int64_t B = a.B, H = a.H, N = a.N, d = a.d;
-  if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
+  const int64_t Nk = a.Nk == 0 ? N : a.Nk;  // key rows per head (0: as many as queries)
+  if (B < 0 || H < 0 || N < 0 || Nk < 0 || d < 0) return ATTN_ERR_SHAPE;
   if (a.dtype != ATTN_DTYPE_F32 && a.dtype != ATTN_DTYPE_F16 && a.dtype != ATTN_DTYPE_BF16)
     return ATTN_ERR_DTYPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
@@ -1534,26 +1544,32 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
   if ((a.flags & ~ATTN_CAUSAL) != 0) return ATTN_ERR_FLAGS;
   if (splits != 0 && (splits < 1 || splits > ATTN_MAX_SPLITS)) return ATTN_ERR_SPLITS;
   if (splits != 0 && (a.flags & ATTN_CAUSAL) != 0) return ATTN_ERR_FLAGS;
-  int64_t bh = 0, bhn = 0, elems = 0;
-  if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &elems))
+  if (Nk != N && (a.flags & ATTN_CAUSAL) != 0) return ATTN_ERR_FLAGS;
+  int64_t bh = 0, bhn = 0, elems = 0, kelems = 0;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &elems) ||
+      !mul_ok(bh, Nk, &kelems) || !mul_ok(kelems, d, &kelems))
     return ATTN_ERR_SHAPE;
   if (bhn == 0) return ATTN_OK;  // empty: nothing to launch
-  if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
+  if (N > ATTN_MAX_N || Nk > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   if (a.q == nullptr || a.k == nullptr || a.v == nullptr || a.o == nullptr)
     return ATTN_ERR_NULLPTR;
   const size_t esize = a.dtype == ATTN_DTYPE_F32 ? 4 : 2;
-  if (elems > INT64_MAX / (int64_t)esize) return ATTN_ERR_SHAPE;
+  if (elems > INT64_MAX / (int64_t)esize || kelems > INT64_MAX / (int64_t)esize)
+    return ATTN_ERR_SHAPE;
   int64_t nblocks = 0;  // the largest grid: 128 query rows per block
   if (!mul_ok(bh, (N + 127) / 128, &nblocks) || nblocks > INT32_MAX) return ATTN_ERR_SHAPE;
   if (H > INT32_MAX) return ATTN_ERR_SHAPE;
 
-  // strides: all zero means contiguous [B, H, N, d]
+  // strides: all zero means contiguous [B, H, rows, d]; q and o have N rows
+  // per head, k and v Nk
   int64_t st[4][3];
   const int64_t* given[4] = {a.q_stride, a.k_stride, a.v_stride, a.o_stride};
+  const int64_t rows[4] = {N, Nk, Nk, N};
   for (int t = 0; t < 4; ++t) {
     const int64_t* g = given[t];
+    const int64_t R = rows[t];
     if (g[0] == 0 && g[1] == 0 && g[2] == 0) {
-      st[t][0] = H * N * d, st[t][1] = N * d, st[t][2] = d;
+      st[t][0] = H * R * d, st[t][1] = R * d, st[t][2] = d;
     } else {
       for (int i = 0; i < 3; ++i) {
         if (g[i] < 0 || g[i] % 8 != 0 || g[i] > INT64_MAX / 4) return ATTN_ERR_LAYOUT;
@@ -1563,12 +1579,12 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
       // the whole tensor must be addressable: sum of (dim - 1) * stride
       int64_t x = 0, y = 0, z = 0;
       if (!mul_ok(B - 1, st[t][0], &x) || !mul_ok(H - 1, st[t][1], &y) ||
-          !mul_ok(N - 1, st[t][2], &z) || x > INT64_MAX / 4 - y - z - d)
+          !mul_ok(R - 1, st[t][2], &z) || x > INT64_MAX / 4 - y - z - d)
         return ATTN_ERR_LAYOUT;
     }
     // the kernels address a head's rows with 32-bit byte offsets
     int64_t head_bytes = 0;
-    if (!mul_ok(N, st[t][2], &head_bytes) || !mul_ok(head_bytes, (int64_t)esize, &head_bytes) ||
+    if (!mul_ok(R, st[t][2], &head_bytes) || !mul_ok(head_bytes, (int64_t)esize, &head_bytes) ||
         head_bytes >= ((int64_t)1 << 31))
       return ATTN_ERR_SHAPE;
   }
@@ -1582,7 +1598,8 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
     return ATTN_ERR_ALIGN;
   uintptr_t r[4][2];
   const void* ptrs[4] = {a.q, a.k, a.v, a.o};
-  for (int t = 0; t < 4; ++t) span_of(ptrs[t], st[t], B, H, N, d, esize, &r[t][0], &r[t][1]);
+  for (int t = 0; t < 4; ++t)
+    span_of(ptrs[t], st[t], B, H, rows[t], d, esize, &r[t][0], &r[t][1]);
   for (int t = 0; t < 3; ++t)
     if (ranges_overlap(r[3][0], r[3][1], r[t][0], r[t][1])) return ATTN_ERR_ALIAS;
   if (a.lse != nullptr) {
@@ -1593,7 +1610,7 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
   int64_t split_len = 0;
   int nsplit = 1;
   if (splits != 0) {
-    split_plan(N, splits, &split_len, &nsplit);
+    split_plan(Nk, splits, &split_len, &nsplit);
     int64_t need = 0;
     if (!mul_ok(bhn, (d + 1) * 4, &need) || !mul_ok(need, nsplit, &need)) return ATTN_ERR_SHAPE;
     if (static_ws) {
@@ -1619,7 +1636,7 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
   Launch x;
   x.stream = reinterpret_cast<hipStream_t>(a.stream);
   x.q = a.q, x.k = a.k, x.v = a.v, x.o = a.o, x.lse = a.lse;
-  x.bh = bh, x.N = N, x.d = d;
+  x.bh = bh, x.N = N, x.nk = Nk, x.d = d;
   x.c2 = a.scale * kLog2e;
   x.L.H = (int)H;
   for (int i = 0; i < 3; ++i) {
@@ -1627,6 +1644,7 @@ int run_fwd(const attn_fwd_args_t& a, int splits = 0, void* ws = nullptr, size_t
   }
   x.splits = nsplit;
   x.sp.len = (int)split_len;
+  x.sp.nk = (int)Nk;
   x.sp.opart = splits ? static_cast<float*>(ws) : nullptr;
   x.sp.lpart = splits ? static_cast<float*>(ws) + (size_t)nsplit * bhn * d : nullptr;
   const bool causal = (a.flags & ATTN_CAUSAL) != 0;
@@ -1652,6 +1670,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   memset(&a, 0, sizeof(a));
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
   a.B = B, a.H = H, a.N = N, a.d = d;
+  a.Nk = N;
   a.scale = scale;
   a.dtype = dtype;
   a.stream = stream;
@@ -1663,9 +1682,10 @@ extern "C" int attn_fwd_ex(const attn_fwd_args_t* args) {
   return run_fwd(*args);
 }
 
-extern "C" size_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
-                                             int splits) {
-  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128) || splits < 1 ||
+extern "C" size_t attn_fwd_splitkv_workspace_ex(int64_t B, int64_t H, int64_t N, int64_t Nk,
+                                                int64_t d, int splits) {
+  if (Nk == 0) Nk = N;
+  if (B < 0 || H < 0 || N < 0 || Nk < 0 || (d != 64 && d != 128) || splits < 1 ||
       splits > ATTN_MAX_SPLITS)
     return 0;
   int64_t bh = 0, bhn = 0, per = 0;
@@ -1673,10 +1693,15 @@ extern "C" size_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, in
   if (bhn == 0) return 0;
   int64_t len = 0;
   int nsplit = 1;
-  split_plan(N, splits, &len, &nsplit);
+  split_plan(Nk, splits, &len, &nsplit);
   int64_t total = 0;
   if (!mul_ok(per, nsplit, &total)) return 0;
   return (size_t)total;
+}
+
+extern "C" size_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
+                                             int splits) {
+  return attn_fwd_splitkv_workspace_ex(B, H, N, N, d, splits);
 }
 
 extern "C" int attn_fwd_splitkv(const attn_fwd_args_t* args, int splits, void* workspace,
@@ -1696,14 +1721,14 @@ extern "C" const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULLPTR: return "q, k, v or o is NULL";
-    case ATTN_ERR_SHAPE: return "invalid shape: negative size, overflow, N > ATTN_MAX_N or grid too large";
+    case ATTN_ERR_SHAPE: return "invalid shape: negative size, overflow, N or Nk > ATTN_MAX_N or grid too large";
     case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (need 64 or 128)";
     case ATTN_ERR_DTYPE: return "unknown dtype";
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_ALIAS: return "an output overlaps an input (or lse overlaps o)";
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
-    case ATTN_ERR_FLAGS: return "unknown flag bits, or a flag the split-KV path does not take";
+    case ATTN_ERR_FLAGS: return "unknown flag bits, or causal with the split-KV path or with Nk != N";
     case ATTN_ERR_SPLITS: return "split count out of range (1 .. ATTN_MAX_SPLITS)";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_fwd_splitkv_workspace()";
     case ATTN_ERR_LAYOUT: return "invalid strides: negative, not a multiple of 8 elements, or overlapping output rows";
@@ -1712,4 +1737,4 @@ extern "C" const char* attn_strerror(int code) {
   }
 }
 
-extern "C" int attn_version(void) { return 200; }
+extern "C" int attn_version(void) { return 210; }

@@ -58,6 +58,9 @@ METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of MI355X bf16 MFMA peak
 METRIC_CAUSAL = "attention fwd causal TFLOP/s (4·B·H·d·N(N+1)/2) and % of MI355X bf16 MFMA peak"
 METRIC_BWD = "attention bwd TFLOP/s (10·B·H·N²·d) and % of MI355X bf16 MFMA peak"
 METRIC_BWD_CAUSAL = "attention bwd causal TFLOP/s (10·B·H·d·N(N+1)/2) and % of MI355X bf16 MFMA peak"
+METRIC_DECODE = ("attention decode GB/s (Q, K, V read once, O and lse written once) "
+                 "and % of MI355X HBM peak")
+HBM_PEAK_GBPS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "attention_attn_fwd_07_amd", "csrc", f)
                for f in ("attn_fwd.hip", "attn_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -77,6 +80,23 @@ def algorithmic_bytes(w) -> int:
     return 4 * w.B * w.H * w.N * w.d * w.elem_bytes + 4 * w.B * w.H * w.N
 
 
+def decode_bytes(w: dict) -> int:
+    """Algorithmic bytes of a call with N queries against Nk keys: Q, K and V
+    read once, O and lse written once."""
+    e = 4 if w["dtype"] == "f32" else 2
+    B, H, N, Nk, d = w["B"], w["H"], w["N"], w["Nk"], w["d"]
+    return 2 * B * H * Nk * d * e + 2 * B * H * N * d * e + 4 * B * H * N
+
+
+def decode_splits(w: dict) -> int:
+    """Key splits for a decode-shaped call (few queries, many keys): enough
+    (head, split) blocks for about two per compute unit, at most 64 splits and
+    at most one per 64-key tile."""
+    bh = w["B"] * w["H"]
+    tiles = (w["Nk"] + 63) // 64
+    return max(1, min(64, tiles, -(-512 // bh)))
+
+
 def traffic_for(w):
     """Measured HBM bytes per launch, if counters exist for this exact kernel."""
     try:
@@ -84,7 +104,8 @@ def traffic_for(w):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get("workloads", {}).get(str(w.key))
+    key = w["key"] if isinstance(w, dict) else str(w.key)
+    entry = rec.get("workloads", {}).get(key)
     if not entry or rec.get("kernel_sha256_16") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
@@ -277,6 +298,37 @@ def auto_warmup(launch, min_launches: int, min_seconds: float):
     return n, last / 20
 
 
+def timed_launches(launch, stream, steps, warmup):
+    """W untimed launches (``warmup``, or the automatic warmup), then exactly K
+    (``steps``, or about 1 s of them, at least 200) back to back, bracketed by
+    torch.cuda.synchronize() for the wall clock and by two HIP events on the
+    launch stream for the mean kernel time.  Returns (W, K, kernel ms per
+    launch, wall ms per launch, the clock sampler of the timed region)."""
+    import torch
+    if warmup is not None:
+        W = warmup
+        t_w = time_batch(launch, W) if W > 0 else 0.0
+        per_launch_s = t_w / W if W > 0 else None
+    else:
+        W, per_launch_s = auto_warmup(launch, min_launches=200, min_seconds=0.3)
+    if steps is not None:
+        K = steps
+    else:
+        K = 200 if per_launch_s is None else max(200, min(100000, int(1.0 / per_launch_s)))
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(K):
+            launch()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    return W, K, ev0.elapsed_time(ev1) / K, wall * 1e3 / K, clock
+
+
 def calibrate_copy(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -287,6 +339,88 @@ def calibrate_copy(nbytes: int, reps: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}))
+
+
+def cpu_baseline_decode(w: dict, q, k, v, scale: float, budget_s: float = 10.0):
+    """The oracle on whole heads of the decode workload until the budget is
+    used, as GB/s of the algorithmic bytes of the heads done."""
+    import numpy as np
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    q64, k64, v64 = (t.double().numpy() for t in (q, k, v))
+    heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])]
+    done, t0 = 0, time.perf_counter()
+    for (b, h) in heads:
+        idx = np.stack([np.full(w["N"], b), np.full(w["N"], h), np.arange(w["N"])], axis=1)
+        oracle.attention_rows(q64, k64, v64, scale, idx, workers=cores)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_head = decode_bytes(w) / len(heads)
+    return {"value": round(done * per_head / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads, each {w['N']} query row(s) against all "
+                      f"{w['Nk']} keys; fp64 numpy on {cores} threads; {dt:.2f} s"}
+
+
+def run_decode(args) -> int:
+    """The decode workload through attn_fwd_splitkv: one JSON line in GB/s."""
+    import numpy as np
+    import torch
+
+    import attention_attn_fwd_07_amd as attn
+    import datagen
+
+    w = dict(datagen.DECODE, key="decode")
+    q, k, v = datagen.make_qkv_kv(w["B"], w["H"], w["N"], w["Nk"], w["d"], w["dtype"], w["seed"])
+    scale = float(np.float32(1.0 / np.sqrt(w["d"])))
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    splits = args.splitkv or decode_splits(w)
+    nbytes_ws = attn.splitkv_workspace_size(w["B"], w["H"], w["N"], w["d"], splits, w["Nk"])
+    ws = torch.empty(max(1, nbytes_ws // 4), dtype=torch.float32, device=dev)
+    launch = attn.plan(qd, kd, vd, o, lse, scale, stream, splits=splits, workspace=ws)
+    W, K, kern_ms, ms_per_step, clock = timed_launches(launch, stream, args.steps, args.warmup)
+    dist = per_launch_ms(launch, stream, max(10, min(K, 50)))
+    flushbuf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = per_launch_ms(launch, stream, 20, flush=lambda: flushbuf.fill_(1))
+    del flushbuf
+    nbytes = decode_bytes(w)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    clk = clock.summary(achieved, HBM_PEAK_GBPS)
+    if clk is not None:  # the clock-scaled peak is a compute figure: not for HBM
+        clk["peak_at_clock"] = clk["frac_at_clock"] = None
+    line = {
+        "metric": METRIC_DECODE,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": w["name"], "B": w["B"], "H": w["H"], "N": w["N"],
+                   "Nk": w["Nk"], "d": w["d"], "dtype": w["dtype"], "scale": scale,
+                   "values": "N(0,1)", "mode": f"fwd split-KV S={splits}", "causal": False},
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "kernel_ms": dict({"mean": round(kern_ms, 5)}, **dist, cold=cold),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for(w)},
+        "clock": clk,
+        "kernel_sha256_16": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(w, q, k, v, scale, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def main(argv=None) -> int:
@@ -306,6 +440,9 @@ def main(argv=None) -> int:
                     help="causal variant (flops counted over the N(N+1)/2 visible pairs)")
     ap.add_argument("--splitkv", type=int, default=0, metavar="S",
                     help="forward through attn_fwd_splitkv with S key splits (+ merge)")
+    ap.add_argument("--decode", action="store_true",
+                    help="one query per head against 65536 cached keys (B=1, H=32, d=128, "
+                         "bf16) through the split-KV path; reported in GB/s against HBM")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (dQ, dK, dV) instead of the forward; "
                          "flops counted as 10 B H N^2 d (the five products; N(N+1)/2 pairs "
@@ -333,6 +470,8 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU available", file=sys.stderr)
         return 1
+    if args.decode:
+        return run_decode(args)
     w = datagen.WORKLOADS[args.workload]
     q, k, v = datagen.workload_inputs(w.key)
     dev = torch.device("cuda:0")
@@ -372,30 +511,7 @@ def main(argv=None) -> int:
         launch = attn.plan(qd, kd, vd, o, lse, w.scale, stream, causal=args.causal)
     if args.causal:
         mode += " causal"
-    if args.warmup is not None:
-        W = args.warmup
-        t_w = time_batch(launch, W) if W > 0 else 0.0
-        per_launch_s = t_w / W if W > 0 else None
-    else:
-        W, per_launch_s = auto_warmup(launch, min_launches=200, min_seconds=0.3)
-    if args.steps is not None:
-        K = args.steps
-    else:
-        K = 200 if per_launch_s is None else max(200, min(100000, int(1.0 / per_launch_s)))
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(K):
-            launch()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-
-    kern_ms = ev0.elapsed_time(ev1) / K  # HIP events on the launch stream, K launches
-    ms_per_step = wall * 1e3 / K
+    W, K, kern_ms, ms_per_step, clock = timed_launches(launch, stream, args.steps, args.warmup)
 
     # After the timed region: the per-launch spread, and for the small
     # workloads the same with L2 and the 256 MB Infinity Cache flushed first

@@ -35,7 +35,8 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_grad", "workload_inputs", "TORCH_DTYPE"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_qkv_kv", "make_grad", "workload_inputs",
+           "TORCH_DTYPE", "DECODE"]
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -136,6 +137,40 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int,
                 idx = rng.choice(N, size=n_hot, replace=False)
                 k[b, h, idx, :] *= hot_mult
     return _round_to(q, dtype), _round_to(k, dtype), _round_to(v, dtype)
+
+
+def make_qkv_kv(B: int, H: int, N: int, Nk: int, d: int, dtype: str, seed: int,
+                mult: float = 1.0, hot_frac: float = 0.0, hot_mult: float = 1.0):
+    """``make_qkv`` with a key length of its own: q of shape [B, H, N, d], k and
+    v of shape [B, H, Nk, d], drawn in that order from one generator, hot keys
+    (``floor(hot_frac * Nk)`` per head) drawn after v.  With Nk = N the values
+    are those of ``make_qkv``."""
+    if dtype not in TORCH_DTYPE:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, Nk, d))
+    v = rng.standard_normal((B, H, Nk, d))
+    if mult != 1.0:
+        q *= mult
+        k *= mult
+        v *= mult
+    n_hot = int(math.floor(hot_frac * Nk))
+    if n_hot:
+        for b in range(B):
+            for h in range(H):
+                idx = rng.choice(Nk, size=n_hot, replace=False)
+                k[b, h, idx, :] *= hot_mult
+    return _round_to(q, dtype), _round_to(k, dtype), _round_to(v, dtype)
+
+
+# Decode-shaped inputs: one new query per head scored against a long cache of
+# keys and values (page 3 section 4: in generation each step computes a
+# 1 x seq_len row of scores against the growing K/V cache, which makes memory
+# bandwidth the bottleneck).  The heads and head dimension of the N=16384
+# workload, the 64K length page 3 section 1.1 mentions, bf16, N(0,1) values.
+DECODE = dict(name="decode B1 H32 N1 Nk65536 d128 bf16", B=1, H=32, N=1, Nk=65536, d=128,
+              dtype="bf16", seed=6)
 
 
 def hot_key_indices(B: int, H: int, N: int, d: int, seed: int, hot_frac: float):

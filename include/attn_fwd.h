@@ -13,9 +13,13 @@
  * computed tile by tile with an online softmax (page 1 "Triton hand-written
  * kernels", section 4: running row max m, running exp-sum l, rescaled fp32
  * accumulator), so the N x N score matrix never reaches device memory.
- * Self-attention (queries and keys share N).  attn_fwd is the non-causal
- * call on contiguous tensors; attn_fwd_ex adds the causal variant and element
- * strides, attn_fwd_splitkv splits each head's keys over several blocks.
+ * attn_fwd is the non-causal self-attention call on contiguous tensors
+ * (queries and keys share N); attn_fwd_ex adds the causal variant, element
+ * strides and a key length Nk of its own (j < Nk above: a few queries against
+ * a long key/value history, as when generation scores each new position
+ * against all cached keys, which page 3 section 4 names as the
+ * memory-bandwidth-bound case of inference), and attn_fwd_splitkv splits
+ * each head's keys over several blocks.
  *
  * Everything here is plain C: pointers, sizes and an opaque stream handle.
  */
@@ -42,14 +46,16 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_NULLPTR = -1,  /* q, k, v or o is NULL while B*H*N > 0              */
   ATTN_ERR_SHAPE = -2,    /* a size is negative, or B*H*N*d overflows int64,
-                             or N exceeds ATTN_MAX_N, or the grid is too large */
+                             or N or Nk exceeds ATTN_MAX_N, or the grid is
+                             too large                                          */
   ATTN_ERR_HEAD_DIM = -3, /* d is not 64 or 128                                 */
   ATTN_ERR_DTYPE = -4,    /* dtype is not an attn_dtype_t value                 */
   ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite                           */
   ATTN_ERR_ALIGN = -6,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte  */
   ATTN_ERR_ALIAS = -7,    /* o or lse overlaps an input, or lse overlaps o      */
   ATTN_ERR_HIP = -8,      /* the kernel launch failed (hipGetLastError)         */
-  ATTN_ERR_FLAGS = -9,    /* attn_fwd_ex: unknown bits in flags                 */
+  ATTN_ERR_FLAGS = -9,    /* attn_fwd_ex: unknown bits in flags, or
+                             ATTN_CAUSAL with Nk != N                           */
   ATTN_ERR_LAYOUT = -10,  /* attn_fwd_ex: a stride is negative, not a multiple
                              of 8 elements, or rows of a head overlap           */
   ATTN_ERR_SPLITS = -11,  /* attn_fwd_splitkv: splits not in 1..ATTN_MAX_SPLITS */
@@ -101,7 +107,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 #define ATTN_CAUSAL 1u /* query row i attends keys 0..i only */
 
 /*
- * Arguments of attn_fwd_ex: those of attn_fwd, plus flags and tensor strides.
+ * Arguments of attn_fwd_ex: those of attn_fwd, plus flags, tensor strides and
+ * the key length.
  *
  * flags   : 0, or ATTN_CAUSAL for the causal variant (page 1 section 4 notes
  *           that practical kernels add a causal mask; page 3 section 3's
@@ -116,6 +123,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *           Every stride must be a multiple of 8 (16-byte aligned rows) and
  *           the (b, h, n) rows of o must not overlap.  lse is always
  *           contiguous [B, H, N].
+ * Nk      : key and value rows per head: k and v are [B, H, Nk, d] (with
+ *           their own strides; all-zero strides mean {H*Nk*d, Nk*d, d}),
+ *           q, o and lse keep N rows.  0 means Nk = N (self-attention); a
+ *           softmax over no keys is undefined, so there is no way to ask for
+ *           it.  Any value in 1..ATTN_MAX_N, smaller or larger than N.
+ *           ATTN_CAUSAL requires Nk == N (ATTN_ERR_FLAGS otherwise): the
+ *           pages define the causal mask for one sequence only.
  */
 typedef struct attn_fwd_args {
   const void* q;
@@ -132,6 +146,7 @@ typedef struct attn_fwd_args {
   int64_t v_stride[3];
   int64_t o_stride[3];
   void* stream;
+  int64_t Nk;
 } attn_fwd_args_t;
 
 /*
@@ -153,13 +168,16 @@ int attn_fwd_ex(const attn_fwd_args_t* args);
  * O = sum_s exp(lse_s - lse) O_s: the combination of per-block row maxima
  * and sums that page 3 section 1.1 describes, using the log-sum-exp that
  * page 3 section 5 stores.  Keys are cut at multiples of 64; the split count
- * actually used is the number of non-empty ranges (at most `splits`).
+ * actually used is the number of non-empty ranges (at most `splits`).  With
+ * few query rows and many keys (Nk >> N) this is the way to fill the GPU.
  *
  * args      : as for attn_fwd_ex; flags must not contain ATTN_CAUSAL
  *             (ATTN_ERR_FLAGS).
  * splits    : 1 .. ATTN_MAX_SPLITS (ATTN_ERR_SPLITS otherwise).
  * workspace : device memory of the current device, 16-byte aligned, at least
- *             attn_fwd_splitkv_workspace(B, H, N, d, splits) bytes, owned by
+ *             attn_fwd_splitkv_workspace_ex(B, H, N, Nk, d, splits) bytes
+ *             (attn_fwd_splitkv_workspace(B, H, N, d, splits) when Nk = N),
+ *             owned by
  *             the caller and not overlapping any tensor (ATTN_ERR_NULLPTR,
  *             ATTN_ERR_ALIGN, ATTN_ERR_WORKSPACE, ATTN_ERR_ALIAS).  It holds
  *             fp32 partial results between the two kernels, both queued on
@@ -170,8 +188,12 @@ int attn_fwd_splitkv(const attn_fwd_args_t* args, int splits, void* workspace,
                      size_t workspace_bytes);
 
 /* Bytes of workspace attn_fwd_splitkv needs (splits_used * B*H*N * (d + 1)
- * * 4), or 0 for empty or invalid sizes. */
+ * * 4, where splits_used depends on the key length), or 0 for empty or
+ * invalid sizes.  _ex takes the key length Nk (0 means N); the plain form is
+ * the self-attention case Nk = N. */
 size_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d, int splits);
+size_t attn_fwd_splitkv_workspace_ex(int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d,
+                                     int splits);
 
 /* Size of the library's own device array behind attn_fwd_splitkv_static. */
 #define ATTN_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
@@ -192,8 +214,8 @@ size_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t d, in
  * args, splits : as for attn_fwd_splitkv (the same kernels run, so the result
  *                is bit-identical to attn_fwd_splitkv with the same splits).
  * Returns the codes of attn_fwd_splitkv, minus the workspace ones, plus
- * ATTN_ERR_STATIC_LIMIT when attn_fwd_splitkv_workspace(B, H, N, d, splits)
- * exceeds ATTN_STATIC_WORKSPACE_BYTES; that and every other argument error is
+ * ATTN_ERR_STATIC_LIMIT when attn_fwd_splitkv_workspace_ex(B, H, N, Nk, d,
+ * splits) exceeds ATTN_STATIC_WORKSPACE_BYTES; that and every other argument error is
  * detected before any HIP call.
  *
  * Every call on one device shares that device's array, which keeps the last

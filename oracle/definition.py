@@ -1,6 +1,9 @@
 """The plain definition of attention forward, in float64 (test infrastructure).
 
-What it computes, per batch b, head h and query row i, for keys j < N:
+What it computes, per batch b, head h and query row i < N, for keys j < Nk
+(Nk = N for self-attention; a few queries against a long key/value history,
+Nk > N, is how generation scores each new position against all cached keys,
+the bandwidth-bound inference case of page 3 section 4):
 
 1. s_ij  = scale * sum_c Q[b,h,i,c] * K[b,h,j,c]
    (page 3, section 3, the decoder layer's scores: Q times K transposed divided
@@ -100,23 +103,35 @@ def _default_workers() -> int:
         return max(1, os.cpu_count() or 1)
 
 
+def _check_shapes(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool) -> None:
+    """q [B, H, N, d], k [B, H, Nk, d], v [B, H, Nk, dv]; Nk >= 1 when N > 0
+    (a softmax over no keys is undefined); causal needs Nk = N."""
+    if (q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or k.shape[:2] != q.shape[:2]
+            or k.shape[3] != q.shape[3] or v.shape[:3] != k.shape[:3]):
+        raise ValueError(f"shape mismatch: q{q.shape} k{k.shape} v{v.shape}")
+    if k.shape[2] == 0 and q.shape[2] > 0 and q.shape[0] * q.shape[1] > 0:
+        raise ValueError("no keys: the softmax over an empty row is undefined")
+    if causal and k.shape[2] != q.shape[2]:
+        raise ValueError("the causal mask is defined for equal query and key lengths")
+
+
 def attention(q, k, v, scale: float, *, causal: bool = False, workers: int | None = None,
               row_chunk: int = ROW_CHUNK):
-    """O and lse for q, k, v of shape [B, H, N, d] (any float input dtype).
+    """O and lse for q [B, H, N, d], k [B, H, Nk, d], v [B, H, Nk, dv] (any
+    float input dtype; Nk = N for self-attention).
 
-    ``causal``: query row i attends keys 0..i only.
+    ``causal``: query row i attends keys 0..i only (needs Nk = N).
 
-    Returns (o, lse): float64 arrays of shape [B, H, N, d] and [B, H, N].
+    Returns (o, lse): float64 arrays of shape [B, H, N, dv] and [B, H, N].
     Work is split into (b, h, row-chunk) tasks on a thread pool with BLAS held
     to one thread per task; every task evaluates the same plain definition.
     """
     q = _as64(q)
     k = _as64(k)
     v = _as64(v)
-    if q.ndim != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
-        raise ValueError(f"shape mismatch: q{q.shape} k{k.shape} v{v.shape}")
+    _check_shapes(q, k, v, causal)
     B, H, N, _ = q.shape
-    o = np.empty(v.shape, dtype=np.float64)
+    o = np.empty((B, H, N, v.shape[3]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     if N == 0:
         return o, lse
@@ -148,6 +163,7 @@ def attention_rows(q, k, v, scale: float, index, *, causal: bool = False,
     q = _as64(q)
     k = _as64(k)
     v = _as64(v)
+    _check_shapes(q, k, v, causal)
     index = np.asarray(index, dtype=np.int64).reshape(-1, 3)
     R = index.shape[0]
     o = np.empty((R, v.shape[-1]), dtype=np.float64)

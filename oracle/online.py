@@ -32,14 +32,18 @@ import numpy as np
 
 
 def attention_online(q, k, v, scale: float, block_n: int, causal: bool = False):
-    """O, lse for q, k, v [B, H, N, d] via the blockwise online recurrence."""
+    """O, lse for q [B, H, N, d], k [B, H, Nk, d], v [B, H, Nk, dv] via the
+    blockwise online recurrence over the Nk keys (causal needs Nk = N)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     if block_n < 1:
         raise ValueError("block_n must be >= 1")
     B, H, N, _ = q.shape
-    o = np.empty(v.shape, dtype=np.float64)
+    Nk = k.shape[2]
+    if causal and Nk != N:
+        raise ValueError("the causal mask is defined for equal query and key lengths")
+    o = np.empty((B, H, N, v.shape[3]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
@@ -47,8 +51,8 @@ def attention_online(q, k, v, scale: float, block_n: int, causal: bool = False):
             m = np.full(N, -np.inf)
             l = np.zeros(N)
             acc = np.zeros((N, vh.shape[1]))
-            for j0 in range(0, N, block_n):
-                j1 = min(N, j0 + block_n)
+            for j0 in range(0, Nk, block_n):
+                j1 = min(Nk, j0 + block_n)
                 s = float(scale) * (qh @ kh[j0:j1].T)
                 if causal:
                     s[np.arange(j0, j1)[None, :] > np.arange(N)[:, None]] = -np.inf

@@ -107,11 +107,12 @@ FLAGS, LAYOUT = -9, -10
 
 
 def ex_args(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=128, d=64, scale=0.125, dtype=BF16,
-            flags=0, qs=(0, 0, 0), ks=(0, 0, 0), vs=(0, 0, 0), os_=(0, 0, 0)):
+            flags=0, qs=(0, 0, 0), ks=(0, 0, 0), vs=(0, 0, 0), os_=(0, 0, 0), Nk=0):
     from attention_attn_fwd_07_amd import _Args
     a = _Args()
     a.q, a.k, a.v, a.o, a.lse = q, k, v, o, lse
     a.B, a.H, a.N, a.d, a.scale, a.dtype, a.flags = B, H, N, d, scale, dtype, flags
+    a.Nk = Nk
     a.q_stride[:], a.k_stride[:], a.v_stride[:], a.o_stride[:] = qs, ks, vs, os_
     a.stream = None
     return a
@@ -166,6 +167,22 @@ def test_ex_null_args(lib):
     (dict(q=None, flags=1), NULLPTR),
 ])
 def test_ex_rejects_before_any_hip_call(lib, kw, code):
+    assert call_ex(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nk=-1), SHAPE), (dict(Nk=(1 << 22) + 1), SHAPE),
+    # the causal mask is defined for one sequence length only
+    (dict(Nk=4096, flags=1), FLAGS), (dict(N=1, Nk=128, flags=1), FLAGS),
+    # k spans its own Nk rows: 2 heads x 4096 keys x 64 x 2 bytes = 1 MiB from K,
+    # so an o placed half-way through it aliases k (it would not with Nk = N)
+    (dict(Nk=4096, o=K + (1 << 19)), ALIAS), (dict(Nk=4096, lse=K + (1 << 19)), ALIAS),
+    # k's explicit strides are checked over Nk rows: a head of 2^20 keys with a
+    # row stride of 2048 elements is beyond 32-bit byte offsets
+    (dict(N=16, Nk=1 << 20, ks=(0, 0, 2048), **{"k": 1 << 40}), SHAPE),
+    (dict(N=0, Nk=4096), OK), (dict(B=0, Nk=-5), SHAPE),
+])
+def test_ex_key_length_rejects_before_any_hip_call(lib, kw, code):
     assert call_ex(lib, **kw) == code
 
 
@@ -255,6 +272,27 @@ def test_workspace_size_zero_for_invalid(lib, args):
     assert ws_size(lib, *args) == 0
 
 
+def ws_size_ex(lib, B, H, N, Nk, d, splits):
+    lib.attn_fwd_splitkv_workspace_ex.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
+    lib.attn_fwd_splitkv_workspace_ex.restype = ctypes.c_size_t
+    return lib.attn_fwd_splitkv_workspace_ex(B, H, N, Nk, d, splits)
+
+
+@pytest.mark.parametrize("B,H,N,Nk,d,splits,used", [
+    (1, 32, 1, 65536, 128, 16, 16), (2, 8, 4, 1000, 64, 7, 6),   # 16 key tiles -> 6 splits
+    (1, 2, 3000, 100, 64, 8, 2), (1, 1, 1, 1, 128, 5, 1)])
+def test_workspace_size_ex_counts_splits_of_the_keys(lib, B, H, N, Nk, d, splits, used):
+    # partial results are per query row; the number of splits follows the keys
+    assert ws_size_ex(lib, B, H, N, Nk, d, splits) == used * B * H * N * (d + 1) * 4
+
+
+def test_workspace_size_ex_zero_key_length_means_n(lib):
+    for (B, H, N, d, splits) in [(1, 8, 65536, 64, 4), (2, 3, 1000, 128, 7), (1, 1, 0, 64, 2)]:
+        assert ws_size_ex(lib, B, H, N, 0, d, splits) == ws_size(lib, B, H, N, d, splits)
+        assert ws_size_ex(lib, B, H, N, N, d, splits) == ws_size(lib, B, H, N, d, splits)
+    assert ws_size_ex(lib, 1, 1, 10, -1, 64, 2) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(splits=0), SPLITS), (dict(splits=65), SPLITS), (dict(splits=-2), SPLITS),
     (dict(flags=1), FLAGS),
@@ -262,6 +300,9 @@ def test_workspace_size_zero_for_invalid(lib, args):
     (dict(ws_bytes=4 * 2 * 128 * 65 * 2 - 4), WORKSPACE),  # 2 tiles -> 2 splits used
     (dict(ws=O), ALIAS), (dict(ws=L - 1024 * 16), ALIAS), (dict(ws=Q + 64), ALIAS),
     (dict(N=0), OK), (dict(N=0, ws=None), OK),
+    # one query row against 4096 keys: 64 key tiles, 4 splits of one row each
+    (dict(N=1, Nk=4096, ws_bytes=4 * 2 * 1 * 65 * 4 - 4, k=1 << 40, v=2 << 40), WORKSPACE),
+    (dict(N=1, Nk=4096, flags=1, k=1 << 40, v=2 << 40), FLAGS),
 ])
 def test_splitkv_rejects_before_any_hip_call(lib, kw, code):
     assert call_split(lib, **kw) == code

@@ -85,6 +85,35 @@ def test_bench_json_line(extra, capsys):
         assert d["metric"].startswith("attention bwd")
 
 
+def test_decode_bytes_and_splits():
+    w = datagen.DECODE
+    assert (w["B"], w["H"], w["N"], w["Nk"], w["d"], w["dtype"]) == (1, 32, 1, 65536, 128, "bf16")
+    # K and V read once (bf16), Q read and O written once, lse written once (fp32)
+    assert bench.decode_bytes(w) == 2 * 32 * 65536 * 128 * 2 + 2 * 32 * 128 * 2 + 4 * 32
+    assert bench.decode_splits(w) == 16                      # 32 heads x 16 = 512 blocks
+    assert bench.decode_splits(dict(w, B=64)) == 1           # 2048 heads fill the GPU alone
+    assert bench.decode_splits(dict(w, H=1, Nk=300)) == 5    # at most one split per key tile
+    assert bench.decode_splits(dict(w, H=1)) == 64
+
+
+def test_cpu_baseline_decode_times_the_oracle():
+    w = dict(datagen.DECODE, Nk=4096, H=4)
+    q, k, v = datagen.make_qkv_kv(w["B"], w["H"], w["N"], w["Nk"], w["d"], w["dtype"], 1)
+    cb = bench.cpu_baseline_decode(w, q, k, v, 0.088, budget_s=0.05)
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["value"] > 0
+    assert "of 4 heads" in cb["sample"]
+
+
+@pytest.mark.gpu
+def test_bench_decode_json_line(capsys):
+    assert bench.main(["--decode", "--steps", "3", "--warmup", "1", "--no-cpu-baseline"]) == 0
+    d = json.loads([x for x in capsys.readouterr().out.splitlines() if x.strip()][-1])
+    assert d["unit"] == "GB/s" and d["steps"] == 3 and d["config"]["Nk"] == 65536
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0.0 < r["achieved"] < 8000.0
+    assert math.isclose(r["frac"], r["achieved"] / r["peak"], rel_tol=1e-3, abs_tol=1e-4)
+
+
 def test_parse_sclk_reads_the_current_level():
     assert bench.parse_sclk("0: 500Mhz\n1: 1650Mhz *\n2: 2400Mhz\n") == 1650.0
     assert bench.parse_sclk("S: 94Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 94.0

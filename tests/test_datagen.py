@@ -64,3 +64,17 @@ def test_make_grad_is_seeded_and_independent_of_qkv():
     q, k, v = datagen.make_qkv(1, 2, 33, 64, "bf16", seed=5)
     assert torch.equal(g1, g2) and g1.dtype == torch.bfloat16 and g1.is_contiguous()
     assert not torch.equal(g1, q) and not torch.equal(g1, v)
+
+
+def test_make_qkv_kv_shapes_and_self_attention_case():
+    q, k, v = datagen.make_qkv_kv(2, 3, 5, 70, 64, "bf16", seed=8, hot_frac=0.1, hot_mult=8.0)
+    assert q.shape == (2, 3, 5, 64) and k.shape == v.shape == (2, 3, 70, 64)
+    # with Nk = N the values are exactly those of make_qkv
+    a = datagen.make_qkv(2, 3, 40, 64, "f16", seed=8, hot_frac=0.05, hot_mult=8.0)
+    b = datagen.make_qkv_kv(2, 3, 40, 40, 64, "f16", seed=8, hot_frac=0.05, hot_mult=8.0)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    # hot keys are counted from the key length: 7 of 70 rows per head are x8
+    _, kp, _ = datagen.make_qkv_kv(2, 3, 5, 70, 64, "f32", seed=8)
+    _, kh, _ = datagen.make_qkv_kv(2, 3, 5, 70, 64, "f32", seed=8, hot_frac=0.1, hot_mult=8.0)
+    changed = (~np.all(kh.numpy() == kp.numpy(), axis=-1)).sum(axis=-1)
+    assert np.all(changed == 7)

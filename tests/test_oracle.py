@@ -207,11 +207,79 @@ def pin_online_matches(attn):
         o2, lse2 = attention_online(q, k, v, 0.6, bn)
         np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(lse, lse2, rtol=1e-13, atol=1e-12)
+    for (N, Nk, bn) in [(1, 130, 64), (7, 50, 16), (40, 9, 4)]:  # key length of its own
+        r = np.random.default_rng(200 + N)
+        q, k, v = (r.standard_normal((1, 2, n, 8)) for n in (N, Nk, Nk))
+        k[..., ::9, :] *= 8.0
+        o, lse = attn(q, k, v, 0.6)
+        o2, lse2 = attention_online(q, k, v, 0.6, bn)
+        np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, lse2, rtol=1e-13, atol=1e-12)
+
+
+# --- query and key lengths that differ (N queries against Nk keys) --------
+
+def _rand_kv(B, H, N, Nk, d, seed):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((B, H, N, d)), r.standard_normal((B, H, Nk, d)),
+            r.standard_normal((B, H, Nk, d)))
+
+
+def pin_cross_brute_force(attn):
+    """Pure-Python textbook softmax of every row, over all Nk keys."""
+    for (N, Nk, d, seed) in [(1, 1, 4, 30), (1, 7, 4, 31), (3, 17, 8, 32), (17, 3, 8, 33),
+                             (2, 40, 1, 34)]:
+        q, k, v = _rand_kv(1, 2, N, Nk, d, seed)
+        o, lse = attn(q, k, v, 0.8)
+        assert o.shape == (1, 2, N, d) and lse.shape == (1, 2, N)
+        for h in range(2):
+            K, V = k[0, h].tolist(), v[0, h].tolist()
+            for i in range(N):
+                ob, lb = _brute_row(q[0, h, i].tolist(), K, V, 0.8)
+                np.testing.assert_allclose(o[0, h, i], ob, rtol=1e-12, atol=1e-12)
+                assert abs(lse[0, h, i] - lb) <= 1e-12 * max(1.0, abs(lb))
+
+
+def pin_cross_sdpa(attn):
+    """torch's SDPA in float64 with different query and key lengths."""
+    for (B, H, N, Nk, d, seed, scale) in [(2, 3, 1, 90, 16, 35, 0.25), (1, 2, 70, 9, 64, 36, 0.125),
+                                          (1, 1, 5, 130, 8, 37, -0.5)]:
+        q, k, v = _rand_kv(B, H, N, Nk, d, seed)
+        o, lse = attn(q, k, v, scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+        ref_lse = torch.logsumexp(scale * (tq @ tk.transpose(-1, -2)), dim=-1)
+        np.testing.assert_allclose(o, ref.numpy(), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_cross_closed_forms(attn):
+    """One query against Nk keys: scale 0 gives mean(V) over the Nk keys and
+    lse = ln Nk; identical keys give the same mean; rows are those of the
+    self-attention result over Nk queries whose first rows are these queries
+    (query rows are independent), tying the cross case to the square one."""
+    N, Nk, d = 3, 41, 8
+    q, k, v = _rand_kv(2, 1, N, Nk, d, 38)
+    mean_v = v.mean(axis=2, keepdims=True)
+    o, lse = attn(q, k, v, 0.0)
+    np.testing.assert_allclose(o, np.broadcast_to(mean_v, o.shape), atol=1e-13)
+    np.testing.assert_allclose(lse, math.log(Nk), atol=1e-13)
+    same = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    o, lse = attn(q, same, v, 0.7)
+    np.testing.assert_allclose(o, np.broadcast_to(mean_v, o.shape), atol=1e-13)
+    s0 = 0.7 * (q @ same[:, :, :1].swapaxes(-1, -2))[..., 0]
+    np.testing.assert_allclose(lse, s0 + math.log(Nk), atol=1e-12)
+    full = np.concatenate([q, np.random.default_rng(39).standard_normal((2, 1, Nk - N, d))],
+                          axis=2)
+    o, lse = attn(q, k, v, 0.6)
+    of, lf = attn(full, k, v, 0.6)
+    np.testing.assert_allclose(o, of[:, :, :N], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lf[:, :, :N], rtol=1e-14, atol=1e-14)
 
 
 PINS = [pin_golden, pin_brute_force, pin_sdpa, pin_rows_sum_to_one, pin_identical_keys,
         pin_constant_v, pin_scale_zero, pin_single_key, pin_dominant_key, pin_invariances,
-        pin_online_matches]
+        pin_online_matches, pin_cross_brute_force, pin_cross_sdpa, pin_cross_closed_forms]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -336,6 +404,14 @@ def _mut_v_shifted(q, k, v, scale):
     return (p @ v) / l, m[:, 0] + np.log(l[:, 0])
 
 
+def _mut_keys_cut_to_queries(q, k, v, scale):
+    # confuses the key count with the query count (invisible when they are equal)
+    k, v = k[:q.shape[0]], v[:q.shape[0]]
+    s = scale * (q @ k.T)
+    m = s.max(1, keepdims=True); p = np.exp(s - m); l = p.sum(1, keepdims=True)
+    return (p @ v) / l, m[:, 0] + np.log(l[:, 0])
+
+
 def _mut_sqrt_scale(q, k, v, scale):
     s = math.sqrt(abs(scale)) * (q @ k.T)
     m = s.max(1, keepdims=True); p = np.exp(s - m); l = p.sum(1, keepdims=True)
@@ -345,7 +421,7 @@ def _mut_sqrt_scale(q, k, v, scale):
 MUTANTS = [_mut_no_scale, _mut_scale_squared, _mut_transposed_scores, _mut_max_wrong_axis,
            _mut_sum_wrong_axis, _mut_exp_sign, _mut_no_max_subtraction, _mut_unnormalised,
            _mut_lse_without_max, _mut_lse_log2, _mut_drop_last_key, _mut_v_shifted,
-           _mut_sqrt_scale]
+           _mut_sqrt_scale, _mut_keys_cut_to_queries]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda m: m.__name__)
@@ -514,3 +590,25 @@ def test_causal_planted_mistakes_are_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"no causal pin caught {name}"
+
+
+def test_cross_length_shape_rules():
+    """N queries against Nk keys: o and lse follow q; no keys, a causal mask
+    over unequal lengths and mismatched k/v rows are refused."""
+    q, k, v = _rand_kv(1, 2, 3, 11, 4, 40)
+    o, lse = oracle.attention(q, k, v, 0.5)
+    assert o.shape == (1, 2, 3, 4) and lse.shape == (1, 2, 3)
+    with pytest.raises(ValueError):
+        oracle.attention(q, k[:, :, :0], v[:, :, :0], 0.5)
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, 0.5, causal=True)
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v[:, :, :5], 0.5)
+    with pytest.raises(ValueError):
+        oracle.attention_rows(q, k, v, 0.5, [[0, 0, 0]], causal=True)
+    with pytest.raises(ValueError):
+        attention_online(q, k, v, 0.5, 4, causal=True)
+    idx = np.array([[0, 1, 2], [0, 0, 0]])
+    orow, lrow = oracle.attention_rows(q, k, v, 0.5, idx)
+    np.testing.assert_allclose(orow, o[0, [1, 0], [2, 0]], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lrow, lse[0, [1, 0], [2, 0]], rtol=1e-15, atol=1e-15)

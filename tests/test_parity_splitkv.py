@@ -44,8 +44,11 @@ def splitkv_parity(q, k, v, scale, dtype, splits, what, kernel=None, monkeypatch
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 64), ("f32", 128),
                                      ("bf16", 64), ("f16", 128)])
 @pytest.mark.parametrize("N,splits", [(1, 3), (63, 2), (64, 4), (65, 2), (1000, 3), (1000, 64),
-                                      (2049, 7)])
+                                      (2049, 7), (1000, 1), (200, 1)])
 def test_splitkv_shapes(dtype, d, N, splits):
+    """Shapes and split counts, among them a single split on grids where the
+    plain path would split keys inside each block (the split-KV path must
+    still write the partial results its merge reads)."""
     q, k, v = datagen.make_qkv(1, 2, N, d, dtype, seed=600 + N + splits)
     splitkv_parity(q, k, v, 1.0 / math.sqrt(d), dtype, splits,
                    f"splitkv {dtype} d={d} N={N} splits={splits}")

@@ -1274,6 +1274,281 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_mfma32(
 }
 
 // ---------------------------------------------------------------------------
+// decode kernel: a few query rows against many keys
+// ---------------------------------------------------------------------------
+//
+// With at most four query rows per head (generation: each new position scored
+// against the whole cache of keys and values, which page 3 section 4 names as
+// the memory-bandwidth-bound case of inference) an MFMA tile of 32 query rows
+// would be almost all padding, and the time is that of reading K and V once.
+// This kernel streams them with plain coalesced 16-byte loads and computes
+// on the VALU:
+//   * a group of LPR lanes holds one key (or value) row, each lane PPL
+//     16-byte pieces of it; a wave covers G = 64 / LPR rows per load and keeps
+//     U rows per group in flight (8 loads of 16 bytes per lane for K, 8 for
+//     V);
+//   * a score is the lane's partial dot product (v_dot2 for the 16-bit
+//     types) summed over the group with DPP exchanges (xor 1, xor 2, then the
+//     mirrors within 8 and within 16 lanes), which leaves the identical sum
+//     in every lane of the group;
+//   * each group runs the online softmax (page 1 section 4) over its rows
+//     for each query: running max m, sum l and the lane's EPL columns of the
+//     accumulator;
+//   * at the end the 4 G group states of the block are merged through LDS
+//     with the same exact rescaling as the split-KV merge, and wave 0 writes
+//     the output rows (or, on the split-KV path, the fp32 partial results).
+// The block takes the keys of its split (all keys without one) in steps of
+// 4 waves x G x U rows; rows past the end are loaded from the last valid row
+// and given probability 0.  Non-causal only.
+// (A vector element is copied to a scalar before __builtin_bit_cast: the
+// cast applied to a subscripted element of an ext_vector_type compiled to a
+// read of element 0 for every subscript here.)
+template <class T> struct DecElem;
+template <> struct DecElem<Bf16T> {
+  static constexpr int EP = 8;  // elements per 16 bytes
+  static __device__ __forceinline__ float dot(u32x4 a, u32x4 b, float c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32 ai = a[i], bi = b[i];
+      c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ai),
+                                          __builtin_bit_cast(bf16x2, bi), c, false);
+    }
+    return c;
+  }
+  static __device__ __forceinline__ void widen(u32x4 x, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(x[i] << 16);
+      f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ u32x4 narrow(const float* f) {
+    return (u32x4){Bf16T::pack2(f[0], f[1]), Bf16T::pack2(f[2], f[3]), Bf16T::pack2(f[4], f[5]),
+                   Bf16T::pack2(f[6], f[7])};
+  }
+};
+template <> struct DecElem<F16T> {
+  static constexpr int EP = 8;
+  static __device__ __forceinline__ float dot(u32x4 a, u32x4 b, float c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32 ai = a[i], bi = b[i];
+      c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, ai), __builtin_bit_cast(f16x2, bi), c,
+                                 false);
+    }
+    return c;
+  }
+  static __device__ __forceinline__ void widen(u32x4 x, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32 xi = x[i];
+      const f16x2 h = __builtin_bit_cast(f16x2, xi);
+      f[2 * i] = (float)h[0];
+      f[2 * i + 1] = (float)h[1];
+    }
+  }
+  static __device__ __forceinline__ u32x4 narrow(const float* f) {
+    return (u32x4){F16T::pack2(f[0], f[1]), F16T::pack2(f[2], f[3]), F16T::pack2(f[4], f[5]),
+                   F16T::pack2(f[6], f[7])};
+  }
+};
+struct F32T {};
+template <> struct DecElem<F32T> {
+  static constexpr int EP = 4;
+  static __device__ __forceinline__ float dot(u32x4 a, u32x4 b, float c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c = fmaf(__uint_as_float(a[i]), __uint_as_float(b[i]), c);
+    return c;
+  }
+  static __device__ __forceinline__ void widen(u32x4 x, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(x[i]);
+  }
+  static __device__ __forceinline__ u32x4 narrow(const float* f) {
+    return (u32x4){__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                   __float_as_uint(f[3])};
+  }
+};
+
+template <int ES, int D>
+struct GeoDec {
+  static constexpr int ROWB = D * ES;                       // bytes of a K or V row
+  static constexpr int LPR = ROWB / 16 < 16 ? ROWB / 16 : 16;  // lanes per row
+  static constexpr int PPL = ROWB / (16 * LPR);             // 16-byte pieces per lane
+  static constexpr int EPL = PPL * 16 / ES;                 // elements per lane
+  static constexpr int G = 64 / LPR;                        // rows per wave and load
+  static constexpr int U = 8 / PPL;                         // rows per group in flight
+  static constexpr int RB = 4 * G * U;                      // rows per block step
+  static_assert(LPR == 8 || LPR == 16, "group sums cover 8 or 16 lanes");
+};
+
+// The value of another lane of the same row of 16, by a DPP pattern.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of LPR (8 or 16) lanes, the same value in each lane:
+// every step adds a value and its exchange partner's, and a + b == b + a.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f32<0xB1>(x);                            // quad_perm [1,0,3,2]: lane i ^ 1
+  x += dpp_f32<0x4E>(x);                            // quad_perm [2,3,0,1]: lane i ^ 2
+  x += dpp_f32<0x141>(x);                           // row_half_mirror: i <-> 7 - i
+  if constexpr (LPR == 16) x += dpp_f32<0x140>(x);  // row_mirror: i <-> 15 - i
+  return x;
+}
+
+template <class E, class T, int D, int NQ>
+__global__ __launch_bounds__(kThreads) void attn_fwd_dec(const T* __restrict__ Q,
+                                                         const T* __restrict__ K,
+                                                         const T* __restrict__ V,
+                                                         T* __restrict__ O,
+                                                         float* __restrict__ LSE, int N, int nqt,
+                                                         float c2, Layout L, Split sp) {
+  using G = GeoDec<(int)sizeof(T), D>;
+  using X = DecElem<E>;
+  constexpr int LPR = G::LPR, PPL = G::PPL, EPL = G::EPL, GR = G::G, U = G::U;
+  constexpr int NS = NQ * (EPL + 2);  // floats of one lane's state
+  __shared__ float st[4 * 64 * NS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int g = lane / LPR, j = lane % LPR;
+  const int bh = blockIdx.x;
+  (void)nqt;
+
+  // the lane's pieces of the query rows (zero past N)
+  u32x4 qf[NQ][PPL];
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      qf[qi][p] = (u32x4){0u, 0u, 0u, 0u};
+      if (qi < N)
+        qf[qi][p] = *reinterpret_cast<const u32x4*>(Q + L.base(L.q, bh) + (long long)qi * L.q[2] +
+                                                    (j * PPL + p) * (16 / sizeof(T)));
+    }
+
+  const int kb0 = sp.first_key(), nkb = sp.keys();
+  const unsigned char* const Kb = reinterpret_cast<const unsigned char*>(
+      K + L.base(L.k, bh) + (long long)kb0 * L.k[2]) + j * PPL * 16;
+  const unsigned char* const Vb = reinterpret_cast<const unsigned char*>(
+      V + L.base(L.v, bh) + (long long)kb0 * L.v[2]) + j * PPL * 16;
+  const int krs = (int)(L.k[2] * sizeof(T)), vrs = (int)(L.v[2] * sizeof(T));
+
+  float m[NQ], l[NQ], acc[NQ][EPL];
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    m[qi] = -INFINITY;
+    l[qi] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[qi][e] = 0.f;
+  }
+
+  for (int r0 = wave * GR * U; r0 < nkb; r0 += G::RB) {
+    u32x4 kx[U][PPL], vx[U][PPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = min(r0 + u * GR + g, nkb - 1);
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        kx[u][p] = *reinterpret_cast<const u32x4*>(Kb + r * krs + 16 * p);
+        vx[u][p] = *reinterpret_cast<const u32x4*>(Vb + r * vrs + 16 * p);
+      }
+    }
+    float pr[NQ][U];
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+      float s[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) a = X::dot(qf[qi][p], kx[u][p], a);
+        s[u] = r0 + u * GR + g < nkb ? group_sum<LPR>(a) * c2 : -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u]);
+      const float mn = fmaxf(m[qi], mx);
+      const float mr = mn == -INFINITY ? 0.f : mn;  // no finite score yet: all p are 0
+      const float al = fast_exp2(m[qi] - mr);
+      m[qi] = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        pr[qi][u] = fast_exp2(s[u] - mr);
+        ps += pr[qi][u];
+      }
+      l[qi] = fmaf(l[qi], al, ps);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[qi][e] *= al;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[EPL];
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) X::widen(vx[u][p], vf + p * X::EP);
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[qi][e] = fmaf(pr[qi][u], vf[e], acc[qi][e]);
+    }
+  }
+
+  // merge the 4 x GR group states of the block: state (w, g) of query qi
+  // holds m, l (equal in its LPR lanes) and each lane's EPL columns
+  float* const mine = st + (wave * 64 + lane) * NS;
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) mine[qi * (EPL + 2) + e] = acc[qi][e];
+    mine[qi * (EPL + 2) + EPL] = m[qi];
+    mine[qi * (EPL + 2) + EPL + 1] = l[qi];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int qi = lane / LPR;  // wave 0: query qi, column piece j
+  if (qi >= NQ || qi >= N) return;
+  float M = -INFINITY;
+  for (int w = 0; w < 4; ++w)
+    for (int gg = 0; gg < GR; ++gg)
+      M = fmaxf(M, st[(w * 64 + gg * LPR + j) * NS + qi * (EPL + 2) + EPL]);
+  const float Mr = M == -INFINITY ? 0.f : M;
+  float lt = 0.f, o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  for (int w = 0; w < 4; ++w)
+    for (int gg = 0; gg < GR; ++gg) {
+      const float* const x = st + (w * 64 + gg * LPR + j) * NS + qi * (EPL + 2);
+      const float wt = fast_exp2(x[EPL] - Mr);
+      lt = fmaf(wt, x[EPL + 1], lt);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(wt, x[e], o[e]);
+    }
+  const float inv = 1.0f / lt;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] *= inv;
+  const float lse = (M + log2f(lt)) * kLn2;
+  if (sp.len) {
+    const size_t r = ((size_t)blockIdx.y * gridDim.x + bh) * N + qi;
+    float* const op = sp.opart + r * D + j * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<f32x4*>(op + e) = (f32x4){o[e], o[e + 1], o[e + 2], o[e + 3]};
+    if (j == 0) sp.lpart[r] = lse;
+  } else {
+    unsigned char* const op = reinterpret_cast<unsigned char*>(
+        O + L.base(L.o, bh) + (long long)qi * L.o[2]) + j * PPL * 16;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p)
+      *reinterpret_cast<u32x4*>(op + 16 * p) = X::narrow(o + p * X::EP);
+    if (LSE != nullptr && j == 0) LSE[(size_t)bh * N + qi] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // split-KV merge
 // ---------------------------------------------------------------------------
 //
@@ -1402,8 +1677,30 @@ bool use_key_split(int64_t blocks128, int64_t nk, bool causal, bool splitkv) {
   return blocks128 <= kNumCUs;
 }
 
+// The decode kernel: at most four query rows per head, without a causal mask.
+// ATTN_FWD_KERNEL=pingpong|pipelined|pipelined2 force an MFMA kernel instead
+// (=decode, or no setting, leaves this choice).
+bool use_decode(int64_t N, bool causal) {
+  if (causal || N > 4) return false;
+  const char* env = getenv("ATTN_FWD_KERNEL");
+  return env == nullptr || (strcmp(env, "pingpong") != 0 && strcmp(env, "pipelined") != 0 &&
+                            strcmp(env, "pipelined2") != 0);
+}
+
+template <class E, class T>
+int launch_dec(const Launch& a) {
+  auto kern = a.d == 128 ? (a.N == 1   ? attn_fwd_dec<E, T, 128, 1>
+                            : a.N == 2 ? attn_fwd_dec<E, T, 128, 2>
+                                       : attn_fwd_dec<E, T, 128, 4>)
+                         : (a.N == 1   ? attn_fwd_dec<E, T, 64, 1>
+                            : a.N == 2 ? attn_fwd_dec<E, T, 64, 2>
+                                       : attn_fwd_dec<E, T, 64, 4>);
+  return launch<T>(kern, a.bh, kThreads, 1, a);
+}
+
 template <class E, class T, bool C>
 int launch16(const Launch& a) {
+  if (use_decode(a.N, C)) return launch_dec<E, T>(a);
   if (use_pingpong(a.bh * ((a.N + 255) / 256) * a.splits, a.d)) {
     const int64_t nqt = (a.N + 255) / 256;
     auto kern = a.d == 128 ? attn_fwd_pp16<E, 128, C> : attn_fwd_pp16<E, 64, C>;
@@ -1420,6 +1717,7 @@ int launch16(const Launch& a) {
 
 template <bool C>
 int launch32(const Launch& a) {
+  if (use_decode(a.N, C)) return launch_dec<F32T, float>(a);
   const int64_t nqt = (a.N + 127) / 128;
   // Few blocks (at most a quarter of the CUs): split each block's keys over
   // its waves (4 groups of 32-key tiles at d = 64, 2 at d = 128, where the

@@ -20,8 +20,11 @@
 //   * attn_fwd_mfma32 fp32: the same structure on the fp32 MFMA; for grids of
 //                     a few blocks, shorter blocks whose four waves split
 //                     the keys (four key groups at d = 64, two at d = 128);
+//   * attn_fwd_dec    any dtype, at most four query rows per head (decode):
+//                     K and V streamed with plain loads, scores on the VALU;
 //   * attn_merge      the split-KV merge.
-// All take a causal flag, element strides and a key-range split.
+// All take element strides, a key length of their own and a key-range
+// split; the three MFMA kernels also a causal flag.
 //
 // Register layouts (the core of the design).  With the 32x32xK MFMA, the C/D
 // fragment of lane l holds column (l % 32) and rows 8*(r/4) + 4*(l/32) + r%4
@@ -1585,10 +1588,14 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* __restr
   const int c = 4 * ((int)threadIdx.x % TPR);
   const size_t plane = (size_t)nbh * N;
   if (r >= (long long)plane) return;
+  // (both loops unrolled so that eight splits' loads are in flight at once:
+  // with few rows the merge is a chain of memory latencies)
   float mx = -INFINITY;
+#pragma unroll 8
   for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, lpart[sp * plane + r]);
   float sum = 0.f;
   f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
   for (int sp = 0; sp < S; ++sp) {
     const size_t rs = sp * plane + r;
     const float w = fast_exp2((lpart[rs] - mx) * kLog2e);

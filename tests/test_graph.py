@@ -85,6 +85,37 @@ def test_splitkv_graph_replays():
         assert torch.equal(lse_g, lse), f"replay {r}: lse differs from the eager call"
 
 
+def test_decode_splitkv_graph_replays():
+    """One query per head against 3000 keys (the decode kernel) through the
+    split-KV path, captured and replayed."""
+    B, H, N, Nk, d, S = 2, 4, 1, 3000, 128, 8
+    q, k, v = (t.to("cuda") for t in datagen.make_qkv_kv(B, H, N, Nk, d, "bf16", 13))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(aa.splitkv_workspace_size(B, H, N, d, S, Nk) // 4, dtype=torch.float32,
+                     device="cuda")
+    scale = d ** -0.5
+    aa.plan(q, k, v, o, lse, scale, splits=S, workspace=ws)()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        aa.plan(q, k, v, o, lse, scale, splits=S, workspace=ws)()
+    for r in range(REPLAYS):
+        fresh = datagen.make_qkv_kv(B, H, N, Nk, d, "bf16", 300 + r)
+        for b, f in zip((q, k, v), fresh):
+            b.copy_(f.to("cuda"))
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, lse_g = o.clone(), lse.clone()
+        o.zero_()
+        lse.zero_()
+        ws.zero_()
+        aa.plan(q, k, v, o, lse, scale, splits=S, workspace=ws)()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o), f"replay {r}: O differs from the eager call"
+        assert torch.equal(lse_g, lse), f"replay {r}: lse differs from the eager call"
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_graph_replays(causal):
     B, H, N, d = 1, 2, 260, 64

@@ -7,7 +7,8 @@ the whole cached history of keys and values, a 1 x Nk row of scores per head
 names it the bandwidth-bound case of inference).  The cases cover one query
 against short, ragged and long key sets, a few queries against many keys, many
 queries against few keys, every kernel the library can pick for the 16-bit
-types, the split-KV path (with a workspace and with the library's static
+types (up to four query rows go to the decode kernel, which streams K and V
+with plain loads and computes on the VALU), the split-KV path (with a workspace and with the library's static
 one), the [B, N, H, d] layout, hot keys, and the decode workload whole
 (B=1, H=32, one query against 65536 keys, d=128, bf16, in the launch
 configuration bench.py times).  Every element of O and lse is compared with
@@ -63,7 +64,7 @@ def _compare(dtype, d, B, H, N, Nk, seed, scale=None, splits=0, static=False, bs
 
 SHAPES = [  # (N, Nk): one query, few queries, more queries than keys
     (1, 1), (1, 63), (1, 64), (1, 65), (1, 1000), (1, 4096),
-    (3, 17), (5, 3000), (17, 2049), (64, 333),
+    (3, 17), (4, 1999), (5, 3000), (17, 2049), (64, 333),
     (300, 77), (1000, 64), (129, 1), (2, 5)]
 
 
@@ -110,6 +111,20 @@ def test_cross_lengths_bshd(dtype, N, Nk, splits):
 def test_cross_lengths_scale_of_either_sign():
     _compare("bf16", 64, 1, 2, 9, 1111, seed=601, scale=-0.3, what="negative scale")
     _compare("f32", 128, 1, 2, 9, 1111, seed=602, scale=0.4, what="scale 0.4")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4])
+def test_decode_kernel_is_deterministic(N):
+    """The same inputs give the same bits, with and without key splits."""
+    attn = _attn()
+    q, k, v = (t.to(DEV) for t in datagen.make_qkv_kv(2, 3, N, 2500, 128, "bf16", 700 + N))
+    o1, l1 = attn.fwd(q, k, v)
+    o2, l2 = attn.fwd(q, k, v)
+    s1, m1 = attn.fwd_splitkv(q, k, v, splits=7)
+    s2, m2 = attn.fwd_splitkv(q, k, v, splits=7)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(s1, s2) and torch.equal(m1, m2)
 
 
 def test_causal_needs_equal_lengths():

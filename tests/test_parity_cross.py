@@ -127,6 +127,33 @@ def test_decode_kernel_is_deterministic(N):
     assert torch.equal(s1, s2) and torch.equal(m1, m2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("splits", [0, 5])
+def test_decode_nan_key_poisons_its_head_only(dtype, splits):
+    """A NaN in one key row of head 0 makes that head's outputs NaN (whole-row
+    IEEE propagation, on both sides) and leaves head 1 finite, with and
+    without key splits: the NaN key sits in one group of one wave of one
+    split, and the block and split merges must carry it."""
+    q, k, v = datagen.make_qkv_kv(1, 2, 2, 3000, 128, dtype, 801)
+    k[0, 0, 1234, 7] = float("nan")
+    o, lse = _run(q, k, v, 0.088, splits=splits)
+    assert np.all(np.isnan(o[0, 0])) and np.all(np.isnan(lse[0, 0]))
+    assert np.all(np.isfinite(o[0, 1])) and np.all(np.isfinite(lse[0, 1]))
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128)])
+def test_decode_longest_key_length(dtype, d):
+    """One query per head against ATTN_MAX_N = 2^22 keys (the largest key
+    length; row offsets up to 2^31 - 256 bytes at d = 128 bf16), plain and
+    with 64 splits, every output against the oracle."""
+    N, Nk = 1, 1 << 22
+    q, k, v = datagen.make_qkv_kv(1, 1, N, Nk, d, dtype, 802)
+    o_ref, lse_ref = oracle.attention(q, k, v, 0.1)
+    for splits in (0, 64):
+        o, lse = _run(q, k, v, 0.1, splits=splits)
+        check(o, lse, o_ref, lse_ref, dtype, f"{dtype} d{d} Nk=2^22 splits={splits}")
+
+
 def test_causal_needs_equal_lengths():
     attn = _attn()
     q, k, v = (torch.zeros(1, 1, n, 64, dtype=torch.bfloat16, device=DEV) for n in (4, 8, 8))

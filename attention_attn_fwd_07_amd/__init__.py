@@ -360,7 +360,7 @@ def bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, workspace, stream=None,
              causal: bool = False) -> None:
     """dQ, dK, dV of O = softmax(scale Q K^T) V into the caller's ``dq``, ``dk``,
-    ``dv`` (contiguous [B, H, N, d], bf16 or fp16), given the forward's ``o``
+    ``dv`` (contiguous [B, H, N, d], q's dtype), given the forward's ``o``
     and ``lse`` and the upstream gradient ``dout``.  Asynchronous on ``stream``."""
     torch = _torch()
     code = _check(q, k, v, o, lse)
@@ -444,7 +444,7 @@ def attention(q, k, v, scale: float | None = None, causal: bool = False):
     ``attn_fwd`` and keeps q, k, v, O and the log-sum-exp; the backward runs
     ``attn_bwd`` on them (page 3 "OpenAI Triton from introduction to model
     practice", section 6: the autograd wrapper saves q, k, v, o and lse for the
-    backward).  Gradients need bf16/fp16 and contiguous q, k, v."""
+    backward).  Gradients need contiguous q, k, v of one length."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     return _attention_fn().apply(q, k, v, float(scale), bool(causal))

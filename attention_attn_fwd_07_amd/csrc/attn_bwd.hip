@@ -10,7 +10,7 @@
 // Like the forward, nothing of size N x N reaches device memory: each block
 // recomputes its tiles of s and P from Q, K and the stored lse.
 //
-// Two kernels:
+// Two kernels (for bf16/fp16; fp32 has its own pair, dq32 and dkdv32, below):
 //   * dq:     one block = 128 query rows (4 waves); it first forms per query
 //             row the pair (lse log2 e, D = rowsum(dO * O)) and stores it in
 //             the workspace for dkdv, then loops over key tiles and
@@ -570,6 +570,206 @@ bool mul_ok_b(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// fp32 backward
+// ---------------------------------------------------------------------------
+//
+// The same two passes for fp32 inputs, on the VALU with LDS tiles (fp32 has no
+// rounding of P or dS to mirror, and no faster matrix path: the fp32 MFMA
+// peak equals the packed fp32 VALU peak).  Tiles of 32 rows; a block of 256
+// threads.  In dq32 thread t owns query row i = t / 8 of the block and, for
+// the 32x32 tiles of S and dP, the keys j = t % 8 + 8u (u < 4); for dQ the
+// columns 4 (t % 8 + 8w) .. +3 (w < D / 32).  dkdv32 is the same with keys and
+// queries exchanged.  Strided row and column assignments keep the threads of
+// a wave on distinct LDS banks; rows are padded by 4 floats for the same
+// reason.
+constexpr int kT32 = 32;  // rows per tile in the fp32 backward
+
+template <int D>
+struct Tile32 {
+  static constexpr int LD = D + 4;  // padded row of an LDS tile, in floats
+};
+
+// Rows r0 .. r0 + 31 of a [rows, D] fp32 tensor (rows >= n read as zero) into
+// an LDS tile, 16 bytes per thread and step.
+template <int D>
+__device__ __forceinline__ void load_tile32(float* __restrict__ dst, const float* __restrict__ src,
+                                            int r0, int n) {
+  constexpr int C4 = D / 4;
+  for (int e = threadIdx.x; e < kT32 * C4; e += 256) {
+    const int r = e / C4, c = (e - r * C4) * 4;
+    f32x4 x = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (r0 + r < n) x = *reinterpret_cast<const f32x4*>(src + (size_t)(r0 + r) * D + c);
+    *reinterpret_cast<f32x4*>(dst + r * Tile32<D>::LD + c) = x;
+  }
+}
+
+// Four dot products of LDS row a with LDS rows b + 8u * LD (u < 4), over D.
+template <int D>
+__device__ __forceinline__ void dot4x(const float* a, const float* b, float (&s)[4]) {
+  constexpr int LD = Tile32<D>::LD;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s[u] = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < D; c += 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a + c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 y = *reinterpret_cast<const f32x4*>(b + 8 * u * LD + c);
+      s[u] = fmaf(x[0], y[0], s[u]);
+      s[u] = fmaf(x[1], y[1], s[u]);
+      s[u] = fmaf(x[2], y[2], s[u]);
+      s[u] = fmaf(x[3], y[3], s[u]);
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dq32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ O, const float* __restrict__ LSE,
+    float2* __restrict__ stats, float* __restrict__ dQ, int N, int nqt, float c2, float scale) {
+  constexpr int LD = Tile32<D>::LD, W = D / 32;
+  __shared__ __attribute__((aligned(16))) float qs[kT32 * LD], gs[kT32 * LD];
+  __shared__ __attribute__((aligned(16))) float ks[kT32 * LD], vs[kT32 * LD];
+  __shared__ float ds[kT32][kT32 + 1];
+  __shared__ float2 st[kT32];
+  const int bh = blockIdx.x / nqt, q0 = (blockIdx.x - bh * nqt) * kT32;
+  const size_t base = (size_t)bh * N * D;
+  const int t = threadIdx.x, i = t >> 3, jg = t & 7;
+  load_tile32<D>(qs, Q + base, q0, N);
+  load_tile32<D>(gs, dO + base, q0, N);
+  // per query row: (lse log2 e, D = sum_c dO O), 8 threads per row
+  {
+    float dd = 0.f;
+    if (q0 + i < N) {
+      const float* orow = O + base + (size_t)(q0 + i) * D;
+      const float* grow = dO + base + (size_t)(q0 + i) * D;
+      for (int c = jg * 4; c < D; c += 32) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(orow + c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(grow + c);
+        dd = fmaf(a[0], b[0], fmaf(a[1], b[1], fmaf(a[2], b[2], fmaf(a[3], b[3], dd))));
+      }
+    }
+    dd += __shfl_xor(dd, 1);
+    dd += __shfl_xor(dd, 2);
+    dd += __shfl_xor(dd, 4);
+    if (jg == 0) {
+      const float2 x = q0 + i < N ? make_float2(LSE[(size_t)bh * N + q0 + i] * kLog2e, dd)
+                                  : make_float2(INFINITY, 0.f);
+      st[i] = x;
+      if (q0 + i < N) stats[(size_t)bh * N + q0 + i] = x;
+    }
+  }
+  float acc[W][4];
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[w][e] = 0.f;
+  const int kend = CAUSAL ? min(N, q0 + kT32) : N;
+  for (int j0 = 0; j0 < kend; j0 += kT32) {
+    __syncthreads();  // previous tile's K, V and dS fully read
+    load_tile32<D>(ks, K + base, j0, N);
+    load_tile32<D>(vs, V + base, j0, N);
+    __syncthreads();
+    float s[4], dp[4];
+    dot4x<D>(qs + i * LD, ks + jg * LD, s);
+    dot4x<D>(gs + i * LD, vs + jg * LD, dp);
+    const float2 x = st[i];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + jg + 8 * u;
+      const bool live = j < N && q0 + i < N && (!CAUSAL || j <= q0 + i);
+      const float p = live ? fast_exp2(s[u] * c2 - x.x) : 0.f;
+      ds[i][jg + 8 * u] = p * (dp[u] - x.y);
+    }
+    __syncthreads();
+    for (int j = 0; j < kT32; ++j) {
+      const float dsv = ds[i][j];
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(ks + j * LD + 4 * (jg + 8 * w));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[w][e] = fmaf(dsv, kv[e], acc[w][e]);
+      }
+    }
+  }
+  if (q0 + i < N) {
+    float* const out = dQ + base + (size_t)(q0 + i) * D;
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      *reinterpret_cast<f32x4*>(out + 4 * (jg + 8 * w)) =
+          (f32x4){acc[w][0] * scale, acc[w][1] * scale, acc[w][2] * scale, acc[w][3] * scale};
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float2* __restrict__ stats, float* __restrict__ dK,
+    float* __restrict__ dV, int N, int nkt, float c2, float scale) {
+  constexpr int LD = Tile32<D>::LD, W = D / 32;
+  __shared__ __attribute__((aligned(16))) float ks[kT32 * LD], vs[kT32 * LD];
+  __shared__ __attribute__((aligned(16))) float qs[kT32 * LD], gs[kT32 * LD];
+  __shared__ float ps[kT32][kT32 + 1], ds[kT32][kT32 + 1];
+  __shared__ float2 st[kT32];
+  const int bh = blockIdx.x / nkt, k0 = (blockIdx.x - bh * nkt) * kT32;
+  const size_t base = (size_t)bh * N * D;
+  const int t = threadIdx.x, j = t >> 3, ig = t & 7;  // key j of the block
+  load_tile32<D>(ks, K + base, k0, N);
+  load_tile32<D>(vs, V + base, k0, N);
+  float dk[W][4], dv[W][4];
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dk[w][e] = dv[w][e] = 0.f;
+  // causal: query rows before k0 see none of these keys
+  for (int i0 = CAUSAL ? k0 : 0; i0 < N; i0 += kT32) {
+    __syncthreads();  // previous tile's Q, dO, P and dS fully read
+    load_tile32<D>(qs, Q + base, i0, N);
+    load_tile32<D>(gs, dO + base, i0, N);
+    if (t < kT32) st[t] = i0 + t < N ? stats[(size_t)bh * N + i0 + t] : make_float2(INFINITY, 0.f);
+    __syncthreads();
+    float s[4], dp[4];
+    dot4x<D>(ks + j * LD, qs + ig * LD, s);   // s[u] = S[query ig + 8u][key j]
+    dot4x<D>(vs + j * LD, gs + ig * LD, dp);  // dP likewise
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int qi = ig + 8 * u;
+      const float2 x = st[qi];
+      const bool live = i0 + qi < N && k0 + j < N && (!CAUSAL || k0 + j <= i0 + qi);
+      const float p = live ? fast_exp2(s[u] * c2 - x.x) : 0.f;
+      ps[qi][j] = p;
+      ds[qi][j] = p * (dp[u] - x.y);
+    }
+    __syncthreads();
+    for (int qi = 0; qi < kT32; ++qi) {
+      const float p = ps[qi][j], d = ds[qi][j];
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const f32x4 g = *reinterpret_cast<const f32x4*>(gs + qi * LD + 4 * (ig + 8 * w));
+        const f32x4 q = *reinterpret_cast<const f32x4*>(qs + qi * LD + 4 * (ig + 8 * w));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dv[w][e] = fmaf(p, g[e], dv[w][e]);
+          dk[w][e] = fmaf(d, q[e], dk[w][e]);
+        }
+      }
+    }
+  }
+  if (k0 + j < N) {
+    float* const ok = dK + base + (size_t)(k0 + j) * D;
+    float* const ov = dV + base + (size_t)(k0 + j) * D;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      *reinterpret_cast<f32x4*>(ok + 4 * (ig + 8 * w)) =
+          (f32x4){dk[w][0] * scale, dk[w][1] * scale, dk[w][2] * scale, dk[w][3] * scale};
+      *reinterpret_cast<f32x4*>(ov + 4 * (ig + 8 * w)) =
+          (f32x4){dv[w][0], dv[w][1], dv[w][2], dv[w][3]};
+    }
+  }
+}
+
 bool overlap_b(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return na > 0 && nb > 0 && x < y + nb && y < x + na;
@@ -602,6 +802,30 @@ int launch_bwd_e(const attn_bwd_args_t& a, float2* stats, int64_t bh) {
   return c ? launch_bwd<E, 64, true>(a, stats, bh) : launch_bwd<E, 64, false>(a, stats, bh);
 }
 
+template <int D, bool C>
+int launch_bwd32(const attn_bwd_args_t& a, float2* stats, int64_t bh) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
+  const float c2 = a.scale * kLog2e;
+  const int64_t nt = (a.N + kT32 - 1) / kT32;
+  const float *q = static_cast<const float*>(a.q), *k = static_cast<const float*>(a.k),
+              *v = static_cast<const float*>(a.v), *dout = static_cast<const float*>(a.dout);
+  hipLaunchKernelGGL((attn_bwd_dq32<D, C>), dim3((unsigned)(bh * nt)), dim3(256), 0, s, q, k, v,
+                     dout, static_cast<const float*>(a.o), a.lse, stats,
+                     static_cast<float*>(a.dq), (int)a.N, (int)nt, c2, a.scale);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  hipLaunchKernelGGL((attn_bwd_dkdv32<D, C>), dim3((unsigned)(bh * nt)), dim3(256), 0, s, q, k,
+                     v, dout, stats, static_cast<float*>(a.dk), static_cast<float*>(a.dv),
+                     (int)a.N, (int)nt, c2, a.scale);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int launch_bwd_f32(const attn_bwd_args_t& a, float2* stats, int64_t bh) {
+  const bool c = (a.flags & ATTN_CAUSAL) != 0;
+  if (a.d == 128) return c ? launch_bwd32<128, true>(a, stats, bh)
+                           : launch_bwd32<128, false>(a, stats, bh);
+  return c ? launch_bwd32<64, true>(a, stats, bh) : launch_bwd32<64, false>(a, stats, bh);
+}
+
 }  // namespace
 
 extern "C" size_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {
@@ -617,17 +841,20 @@ extern "C" int attn_bwd(const attn_bwd_args_t* args, void* ws, size_t ws_bytes) 
   const attn_bwd_args_t& a = *args;
   const int64_t B = a.B, H = a.H, N = a.N, d = a.d;
   if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
-  if (a.dtype != ATTN_DTYPE_F16 && a.dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (a.dtype != ATTN_DTYPE_F16 && a.dtype != ATTN_DTYPE_BF16 && a.dtype != ATTN_DTYPE_F32)
+    return ATTN_ERR_DTYPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(a.scale)) return ATTN_ERR_SCALE;
   if ((a.flags & ~ATTN_CAUSAL) != 0) return ATTN_ERR_FLAGS;
+  const int64_t esize = a.dtype == ATTN_DTYPE_F32 ? 4 : 2;
   int64_t bh = 0, bhn = 0, elems = 0;
   if (!mul_ok_b(B, H, &bh) || !mul_ok_b(bh, N, &bhn) || !mul_ok_b(bhn, d, &elems) ||
-      elems > INT64_MAX / 2)
+      elems > INT64_MAX / esize)
     return ATTN_ERR_SHAPE;
   if (bhn == 0) return ATTN_OK;
-  if (N > ATTN_MAX_N || N * d * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
-  if (bh * ((N + kBM - 1) / kBM) > INT32_MAX || bhn > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (N > ATTN_MAX_N || N * d * esize >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  // the largest grid: 32-row tiles (fp32), 128-row blocks otherwise
+  if (bh * ((N + kT32 - 1) / kT32) > INT32_MAX || bhn > INT32_MAX) return ATTN_ERR_SHAPE;
   const void* ptrs[9] = {a.q, a.k, a.v, a.o, a.dout, a.lse, a.dq, a.dk, a.dv};
   for (const void* p : ptrs)
     if (p == nullptr) return ATTN_ERR_NULLPTR;
@@ -635,7 +862,7 @@ extern "C" int attn_bwd(const attn_bwd_args_t* args, void* ws, size_t ws_bytes) 
   for (int i = 0; i < 9; ++i)
     if ((reinterpret_cast<uintptr_t>(ptrs[i]) & (i == 5 ? 3u : 15u)) != 0) return ATTN_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return ATTN_ERR_ALIGN;
-  const size_t tb = (size_t)elems * 2, lb = (size_t)bhn * 4, wb = (size_t)bhn * 8;
+  const size_t tb = (size_t)elems * esize, lb = (size_t)bhn * 4, wb = (size_t)bhn * 8;
   if (ws_bytes < wb) return ATTN_ERR_WORKSPACE;
   const size_t sizes[9] = {tb, tb, tb, tb, tb, lb, tb, tb, tb};
   // outputs (dq, dk, dv) and the workspace must not overlap anything else
@@ -648,5 +875,6 @@ extern "C" int attn_bwd(const attn_bwd_args_t* args, void* ws, size_t ws_bytes) 
   // --- launch -------------------------------------------------------------
   float2* stats = static_cast<float2*>(ws);
   if (a.dtype == ATTN_DTYPE_BF16) return launch_bwd_e<Bf16T>(a, stats, bh);
-  return launch_bwd_e<F16T>(a, stats, bh);
+  if (a.dtype == ATTN_DTYPE_F16) return launch_bwd_e<F16T>(a, stats, bh);
+  return launch_bwd_f32(a, stats, bh);
 }

@@ -486,9 +486,6 @@ def main(argv=None) -> int:
     pairs = w.N * w.N if not args.causal else w.N * (w.N + 1) // 2  # visible (i, j)
     flops = 4 * w.B * w.H * pairs * w.d
     if args.backward:
-        if w.dtype == "f32":
-            print("bench.py: the backward takes bf16/fp16 only", file=sys.stderr)
-            return 2
         attn.fwd(qd, kd, vd, w.scale, causal=args.causal)  # warm the forward once
         o, lse = attn.fwd(qd, kd, vd, w.scale, causal=args.causal)
         g = datagen.make_grad(w.B, w.H, w.N, w.d, w.dtype, seed=w.key).to(dev)

@@ -36,12 +36,13 @@ extern "C" {
  * lse        : the forward's log-sum-exp output, fp32, for the same scale and
  *              flags.
  * dq, dk, dv : written: the gradients, rounded to nearest-even to `dtype`
- *              from fp32 accumulators.  They must not overlap each other or
+ *              from fp32 accumulators (for fp32, the accumulators).  They must not overlap each other or
  *              any input.
  * B, H, N, d : as for attn_fwd (d = 64 or 128).
  * scale      : the forward's scale, finite.
- * dtype      : ATTN_DTYPE_F16 or ATTN_DTYPE_BF16 (fp32 is not supported by the
- *              backward: ATTN_ERR_DTYPE).
+ * dtype      : ATTN_DTYPE_F16, ATTN_DTYPE_BF16 or ATTN_DTYPE_F32 (fp32 runs
+ *              kernels of its own: VALU products over LDS tiles of 32 rows,
+ *              P and dS kept in fp32).
  * flags      : 0 or ATTN_CAUSAL (query i attends keys 0..i).
  * stream     : a hipStream_t (NULL = the null stream).
  */

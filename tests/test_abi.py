@@ -393,7 +393,7 @@ def test_bwd_workspace_size(lib):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=F32), DTYPE), (dict(dtype=5), DTYPE), (dict(d=96), HEAD_DIM),
+    (dict(dtype=3), DTYPE), (dict(dtype=5), DTYPE), (dict(d=96), HEAD_DIM),
     (dict(scale=float("nan")), SCALE), (dict(flags=4), FLAGS), (dict(N=-1), SHAPE),
     (dict(dq=None), NULLPTR), (dict(lse=None), NULLPTR), (dict(dout=None), NULLPTR),
     (dict(ws=None), NULLPTR), (dict(dk=DK + 8), ALIGN), (dict(lse=LS + 2), ALIGN),

@@ -26,6 +26,12 @@ on output; the products' terms have random signs, so a rounding of the terms
 moves the sum by the same relative RMS as it moves the terms), which gives a
 relative RMS near u.  The bar is 2u: bf16 7.8e-3, fp16 9.8e-4.  A bias such
 as a D off by a percent, or P taken from a wrong lse, exceeds it.
+
+fp32 inputs (their own kernels, nothing rounded below fp32): u = 2^-24 in
+the bound.  Their rel-F bar is set by what 2u leaves out: P is recomputed
+from the forward's fp32 lse, which carries a few ulps of |lse| (about 1e-6
+relative in P), and each product accumulates d or N fp32 terms (RMS near
+sqrt(n) 2^-24, under 1e-6 here); the bar 1e-5 is five times their sum.
 """
 import math
 
@@ -38,8 +44,8 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-RR = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
-RELF = {dt: 2.0 * u for dt, u in RR.items()}
+RR = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -24}
+RELF = {"bf16": 2.0 * RR["bf16"], "f16": 2.0 * RR["f16"], "f32": 1e-5}
 
 
 def _attn():
@@ -112,7 +118,7 @@ def check_grads(q, k, v, g, scale, causal, dtype, what):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 300, 640])
 @pytest.mark.parametrize("causal", [False, True])
@@ -160,11 +166,11 @@ def test_bwd_closed_forms_at_size():
                   <= sum_bound[:, 0])
 
 
-def test_bwd_binding_rejects_fp32_and_missing_lse():
+def test_bwd_binding_rejects_mixed_dtypes_and_missing_lse():
     attn = _attn()
     q = torch.zeros(1, 1, 64, 64, dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
-        attn.bwd(q, q, q, q, torch.zeros(1, 1, 64, device="cuda"), q)
+        attn.bwd(q, q.bfloat16(), q, q, torch.zeros(1, 1, 64, device="cuda"), q)
     qb = q.bfloat16()
     with pytest.raises(ValueError):
         attn.bwd(qb, qb, qb, qb, None, qb)
@@ -213,3 +219,42 @@ def test_bwd_random_case(i):
     q, k, v = datagen.make_qkv(B, H, N, d, dtype, seed=seed)
     g = datagen.make_qkv(B, H, N, d, dtype, seed=seed + 50000)[0]
     check_grads(q, k, v, g, scale, causal, dtype, f"random bwd case {i}")
+
+
+def _bwd_case32(i):
+    rng = np.random.default_rng(9300 + i)
+    d = [64, 128][int(rng.integers(2))]
+    N = int(np.exp(rng.uniform(0.0, math.log(700.0))))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    causal = bool(rng.integers(2))
+    scale = 1.0 / math.sqrt(d) if rng.random() < 0.6 else float(rng.uniform(-0.3, 0.4))
+    return d, N, B, H, causal, scale, 9300 + i
+
+
+@pytest.mark.parametrize("i", range(12), ids=lambda i: "{}-d{}-N{}-B{}H{}-{}".format(
+    i, *_bwd_case32(i)[:4], "causal" if _bwd_case32(i)[4] else "plain"))
+def test_bwd_f32_random_case(i):
+    """fp32 inputs: a seeded sweep of head dim, N, B, H, causal and scale,
+    every gradient element within its bound, rel-F within 1e-5."""
+    d, N, B, H, causal, scale, seed = _bwd_case32(i)
+    q, k, v = datagen.make_qkv(B, H, N, d, "f32", seed=seed)
+    g = datagen.make_qkv(B, H, N, d, "f32", seed=seed + 50000)[0]
+    check_grads(q, k, v, g, scale, causal, "f32", f"random fp32 bwd case {i}")
+
+
+def test_autograd_wrapper_f32():
+    """attention() on fp32 tensors: gradients from the fp32 backward."""
+    attn = _attn()
+    q, k, v = datagen.make_qkv(1, 2, 150, 128, "f32", seed=813)
+    g = datagen.make_grad(1, 2, 150, 128, "f32", seed=813)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev).requires_grad_(True) for t in (q, k, v))
+    o = attn.attention(qd, kd, vd, 0.1, causal=True)
+    o.backward(g.to(dev))
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.attention(q, k, v, 0.1, causal=True)
+    assert np.abs(o.detach().cpu().double().numpy() - o_ref).max() <= 1e-4
+    refs = oracle.attention_backward(q, k, v, g, 0.1, causal=True)
+    for got, ref in zip((qd.grad, kd.grad, vd.grad), refs):
+        got = got.cpu().double().numpy()
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 1e-5

@@ -13,6 +13,7 @@ GPU is present, calls raise.
     attn_fwd_splitkv_static(q, k, v, o, lse, scale, 4)  # no workspace, no allocation
     dq, dk, dv = bwd(q, k, v, o, lse, do)    # gradients (include/attn_bwd.h)
     o = attention(q, k, v)                 # with autograd: o.backward(do) runs attn_bwd
+    o, lse = merge([o1, o2], [lse1, lse2])   # results over two key shards -> over both
 
 Tensors are ``[B, H, N, d]`` fp32/fp16/bf16 with d in {64, 128}; k and v may
 have their own number of rows Nk (``[B, H, Nk, d]``: a few queries against a
@@ -35,7 +36,7 @@ from .build import LIB
 __all__ = ["attn_fwd", "fwd", "plan", "Plan", "attn_strerror", "attn_version", "library_path",
            "AttnError", "ATTN_CAUSAL", "splitkv_workspace_size", "fwd_splitkv", "attn_bwd",
            "bwd", "bwd_workspace_size", "attn_fwd_splitkv_static", "STATIC_WORKSPACE_BYTES",
-           "attention"]
+           "attention", "merge"]
 
 STATIC_WORKSPACE_BYTES = 64 << 20  # ATTN_STATIC_WORKSPACE_BYTES of include/attn_fwd.h
 
@@ -106,6 +107,9 @@ def _load():
     lib.attn_fwd_splitkv_workspace.restype = ctypes.c_size_t
     lib.attn_fwd_splitkv_workspace_ex.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int]
     lib.attn_fwd_splitkv_workspace_ex.restype = ctypes.c_size_t
+    lib.attn_fwd_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, vp, vp,
+                                   i64, i64, i64, i64, ctypes.c_int, vp]
+    lib.attn_fwd_merge.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.POINTER(_BwdArgs), vp, ctypes.c_size_t]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_workspace.argtypes = [i64, i64, i64, i64]
@@ -349,6 +353,48 @@ def fwd(q, k, v, scale: float | None = None, return_lse: bool = True, causal: bo
     lse = (torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
            if return_lse else None)
     attn_fwd(q, k, v, o, lse, scale, causal=causal)
+    return o, lse
+
+
+def merge(o_parts, lse_parts, o=None, lse=None, stream=None):
+    """``attn_fwd_merge``: the results over disjoint key sets (each an O of shape
+    [B, H, N, d] and its fp32 lse [B, H, N], as ``fwd`` returns them for one
+    shard of the keys) combined into the result over all the keys.  Allocates
+    ``o`` and ``lse`` if not given; returns (o, lse)."""
+    torch = _torch()
+    codes = _dtype_codes()
+    if len(o_parts) != len(lse_parts) or not o_parts:
+        raise ValueError("o_parts and lse_parts must be non-empty and of equal length")
+    o0 = o_parts[0]
+    if o0.dtype not in codes or o0.dim() != 4:
+        raise ValueError("each part's O must be a 4-D float32/float16/bfloat16 tensor")
+    for x, l in zip(o_parts, lse_parts):
+        if (x.shape != o0.shape or x.dtype != o0.dtype or x.device != o0.device
+                or not x.is_contiguous()):
+            raise ValueError("every part's O must be contiguous with the first one's shape, "
+                             "dtype and device")
+        if (l is None or l.dtype != torch.float32 or tuple(l.shape) != tuple(o0.shape[:3])
+                or l.device != o0.device or not l.is_contiguous()):
+            raise ValueError("every part needs a contiguous float32 lse of shape [B, H, N]")
+    if o is None:
+        o = torch.empty_like(o0)
+    if lse is None:
+        lse = torch.empty(o0.shape[:3], dtype=torch.float32, device=o0.device)
+    if o.shape != o0.shape or o.dtype != o0.dtype or not o.is_contiguous():
+        raise ValueError("o must be contiguous with the parts' shape and dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(o0.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    n = len(o_parts)
+    optrs = (ctypes.c_void_p * n)(*[x.data_ptr() for x in o_parts])
+    lptrs = (ctypes.c_void_p * n)(*[x.data_ptr() for x in lse_parts])
+    B, H, N, d = (int(x) for x in o0.shape)
+    with torch.cuda.device(o0.device):
+        rc = _load().attn_fwd_merge(optrs, lptrs, n, o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                                    codes[o0.dtype], stream)
+    if rc != ATTN_OK:
+        _raise_for(rc)
     return o, lse
 
 

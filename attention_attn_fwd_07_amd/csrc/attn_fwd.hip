@@ -1613,6 +1613,64 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge(const float* __restr
   if (LSE != nullptr && c == 0) LSE[r] = mx + log2f(sum) * kLn2;
 }
 
+// The merge of caller-supplied partial results (attn_fwd_merge): part s is an
+// O_s in the element type and its lse_s, each a contiguous [B, H, N(, d)]
+// tensor of its own; the same arithmetic as attn_merge.
+struct MergeParts {
+  const void* o[ATTN_MAX_SPLITS];
+  const float* lse[ATTN_MAX_SPLITS];
+};
+struct InF32 {
+  static __device__ __forceinline__ f32x4 load4(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+};
+struct InBf16 {
+  static __device__ __forceinline__ f32x4 load4(const uint16_t* p) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    return (f32x4){__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                   __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
+  }
+};
+struct InF16 {
+  static __device__ __forceinline__ f32x4 load4(const uint16_t* p) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    const u32 x0 = x[0], x1 = x[1];
+    const f16x2 a = __builtin_bit_cast(f16x2, x0), b = __builtin_bit_cast(f16x2, x1);
+    return (f32x4){(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+  }
+};
+
+template <class OUT, class IN, class T, int D>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_parts(MergeParts P, int S,
+                                                                  T* __restrict__ O,
+                                                                  float* __restrict__ LSE,
+                                                                  long long rows) {
+  constexpr int TPR = D / 4, RPB = kMergeThreads / TPR;
+  const long long r = (long long)blockIdx.x * RPB + (int)threadIdx.x / TPR;  // of B*H*N rows
+  const int c = 4 * ((int)threadIdx.x % TPR);
+  if (r >= rows) return;
+  float mx = -INFINITY;
+#pragma unroll 8
+  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, P.lse[sp][r]);
+  float sum = 0.f;
+  f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int sp = 0; sp < S; ++sp) {
+    const float w = fast_exp2((P.lse[sp][r] - mx) * kLog2e);
+    sum += w;
+    const f32x4 x = IN::load4(static_cast<const T*>(P.o[sp]) + r * D + c);
+    o[0] = fmaf(w, x[0], o[0]);
+    o[1] = fmaf(w, x[1], o[1]);
+    o[2] = fmaf(w, x[2], o[2]);
+    o[3] = fmaf(w, x[3], o[3]);
+  }
+  const float inv = 1.0f / sum;
+  o[0] *= inv, o[1] *= inv, o[2] *= inv, o[3] *= inv;
+  OUT::store4(O + r * D + c, o);
+  if (LSE != nullptr && c == 0) LSE[r] = mx + log2f(sum) * kLn2;
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -2020,6 +2078,67 @@ extern "C" int attn_fwd_splitkv_static(const attn_fwd_args_t* args, int splits) 
   if (args == nullptr) return ATTN_ERR_NULLPTR;
   if (splits < 1 || splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
   return run_fwd(*args, splits, nullptr, 0, true);
+}
+
+extern "C" int attn_fwd_merge(const void* const* o_parts, const float* const* lse_parts,
+                              int nparts, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+                              int64_t d, int dtype, void* stream) {
+  // --- validation: no HIP call before this block has passed -------------
+  if (B < 0 || H < 0 || N < 0 || d < 0) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_F16 && dtype != ATTN_DTYPE_BF16)
+    return ATTN_ERR_DTYPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (nparts < 1 || nparts > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
+  int64_t bh = 0, rows = 0, elems = 0;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &rows) || !mul_ok(rows, d, &elems) ||
+      elems > INT64_MAX / 4)
+    return ATTN_ERR_SHAPE;
+  if (rows == 0) return ATTN_OK;
+  if (o_parts == nullptr || lse_parts == nullptr || o == nullptr) return ATTN_ERR_NULLPTR;
+  const size_t esize = dtype == ATTN_DTYPE_F32 ? 4 : 2;
+  const size_t ob = (size_t)elems * esize, lb = (size_t)rows * 4;
+  auto misaligned = [](const void* p, uintptr_t al) {
+    return (reinterpret_cast<uintptr_t>(p) & (al - 1)) != 0;
+  };
+  if (misaligned(o, 16) || (lse != nullptr && misaligned(lse, 4))) return ATTN_ERR_ALIGN;
+  MergeParts P;
+  for (int s = 0; s < nparts; ++s) {
+    if (o_parts[s] == nullptr || lse_parts[s] == nullptr) return ATTN_ERR_NULLPTR;
+    if (misaligned(o_parts[s], 16) || misaligned(lse_parts[s], 4)) return ATTN_ERR_ALIGN;
+    // outputs must not overlap any input
+    if (overlaps(o, ob, o_parts[s], ob) || overlaps(o, ob, lse_parts[s], lb))
+      return ATTN_ERR_ALIAS;
+    if (lse != nullptr && (overlaps(lse, lb, o_parts[s], ob) || overlaps(lse, lb, lse_parts[s], lb)))
+      return ATTN_ERR_ALIAS;
+    P.o[s] = o_parts[s];
+    P.lse[s] = lse_parts[s];
+  }
+  if (lse != nullptr && overlaps(o, ob, lse, lb)) return ATTN_ERR_ALIAS;
+  for (int s = nparts; s < ATTN_MAX_SPLITS; ++s) P.o[s] = nullptr, P.lse[s] = nullptr;
+
+  // --- launch -------------------------------------------------------------
+  const int tpr = (int)d / 4, rpb = kMergeThreads / tpr;
+  const int64_t nblocks = (rows + rpb - 1) / rpb;
+  if (nblocks > INT32_MAX) return ATTN_ERR_SHAPE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)nblocks), block(kMergeThreads);
+  if (dtype == ATTN_DTYPE_BF16) {
+    auto k = d == 128 ? attn_merge_parts<Out16<Bf16T>, InBf16, uint16_t, 128>
+                      : attn_merge_parts<Out16<Bf16T>, InBf16, uint16_t, 64>;
+    hipLaunchKernelGGL(k, grid, block, 0, st, P, nparts, static_cast<uint16_t*>(o), lse,
+                       (long long)rows);
+  } else if (dtype == ATTN_DTYPE_F16) {
+    auto k = d == 128 ? attn_merge_parts<Out16<F16T>, InF16, uint16_t, 128>
+                      : attn_merge_parts<Out16<F16T>, InF16, uint16_t, 64>;
+    hipLaunchKernelGGL(k, grid, block, 0, st, P, nparts, static_cast<uint16_t*>(o), lse,
+                       (long long)rows);
+  } else {
+    auto k = d == 128 ? attn_merge_parts<OutF32, InF32, float, 128>
+                      : attn_merge_parts<OutF32, InF32, float, 64>;
+    hipLaunchKernelGGL(k, grid, block, 0, st, P, nparts, static_cast<float*>(o), lse,
+                       (long long)rows);
+  }
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 extern "C" const char* attn_strerror(int code) {

@@ -226,6 +226,38 @@ size_t attn_fwd_splitkv_workspace_ex(int64_t B, int64_t H, int64_t N, int64_t Nk
  */
 int attn_fwd_splitkv_static(const attn_fwd_args_t* args, int splits);
 
+/*
+ * attn_fwd_merge - combine results over disjoint key sets into the result over
+ * their union (the exact merge of attn_fwd_splitkv, for partial results the
+ * caller computed, e.g. with attn_fwd_ex over shards of a long key/value
+ * cache, one shard per GPU or per call).  Page 3 section 1.1 merges per-block
+ * row maxima and sums into the row's; section 5's stored log-sum-exp makes
+ * that a formula:
+ *
+ *   lse = ln sum_s exp(lse_s),   O = sum_s exp(lse_s - lse) O_s.
+ *
+ * o_parts   : host array of nparts device pointers, each a contiguous
+ *             [B, H, N, d] O_s of element type `dtype`, 16-byte aligned.
+ * lse_parts : host array of nparts device pointers, each a contiguous
+ *             [B, H, N] fp32 lse_s, 4-byte aligned.  Every part must cover at
+ *             least one key (lse_s finite): a row whose parts are all empty
+ *             has no value.
+ * nparts    : 1 .. ATTN_MAX_SPLITS (ATTN_ERR_SPLITS otherwise).
+ * o         : device pointer, contiguous [B, H, N, d], `dtype`; written, O
+ *             rounded to nearest-even from fp32.
+ * lse       : device pointer, [B, H, N] fp32, or NULL to skip it.
+ * B, H, N, d, dtype, stream : as for attn_fwd.
+ *
+ * The host arrays are read during the call only.  Outputs must not overlap
+ * any part (ATTN_ERR_ALIAS) or each other.  Every argument error is detected
+ * before any HIP call; B*H*N == 0 returns ATTN_OK without a launch.  One
+ * kernel on `stream`; nothing is allocated; the result is deterministic and
+ * does not depend on the order of the parts beyond fp32 rounding.
+ */
+int attn_fwd_merge(const void* const* o_parts, const float* const* lse_parts, int nparts,
+                   void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                   void* stream);
+
 /* Static text for a return code (never NULL). */
 const char* attn_strerror(int code);
 

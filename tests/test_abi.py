@@ -339,6 +339,42 @@ def test_splitkv_static_null_args(lib):
 
 
 # ---------------------------------------------------------------------------
+# attn_fwd_merge: argument checks
+# ---------------------------------------------------------------------------
+
+def call_merge(lib, nparts=2, o_parts=None, lse_parts=None, o=O, lse=L, B=1, H=2, N=128, d=64,
+               dtype=BF16, null_arrays=False):
+    vp = ctypes.c_void_p
+    lib.attn_fwd_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, vp, vp,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int, vp]
+    lib.attn_fwd_merge.restype = ctypes.c_int
+    if o_parts is None:
+        o_parts = [(1 + s) << 36 for s in range(max(nparts, 0))]
+    if lse_parts is None:
+        lse_parts = [(100 + s) << 36 for s in range(max(nparts, 0))]
+    n = max(len(o_parts), 1)
+    op = (vp * n)(*o_parts) if not null_arrays else None
+    lp = (vp * n)(*lse_parts) if not null_arrays else None
+    return lib.attn_fwd_merge(op, lp, nparts, o, lse, B, H, N, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nparts=0), SPLITS), (dict(nparts=65), SPLITS), (dict(nparts=-1), SPLITS),
+    (dict(dtype=9), DTYPE), (dict(d=96), HEAD_DIM), (dict(N=-2), SHAPE),
+    (dict(null_arrays=True), NULLPTR), (dict(o=None), NULLPTR),
+    (dict(o_parts=[1 << 36, None]), NULLPTR), (dict(lse_parts=[100 << 36, None]), NULLPTR),
+    (dict(o=O + 8), ALIGN), (dict(lse=L + 2), ALIGN), (dict(o_parts=[(1 << 36) + 8, 2 << 36]), ALIGN),
+    (dict(lse_parts=[(100 << 36) + 2, 101 << 36]), ALIGN),
+    (dict(o=(1 << 36) + 64), ALIAS), (dict(lse=(101 << 36) + 4), ALIAS),
+    (dict(lse=O + 16), ALIAS), (dict(o=(100 << 36) + 16), ALIAS),
+    (dict(N=0), OK), (dict(B=0, null_arrays=True), OK),
+])
+def test_merge_rejects_before_any_hip_call(lib, kw, code):
+    assert call_merge(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
 # attn_bwd: argument checks
 # ---------------------------------------------------------------------------
 

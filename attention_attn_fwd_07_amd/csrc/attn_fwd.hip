@@ -1712,19 +1712,22 @@ int launch(void (*kernel)(const T*, const T*, const T*, T*, float*, int, int, fl
 constexpr int kNumCUs = 256;  // MI355X
 
 // Kernel choice for the 16-bit types: at d = 128 the 8-wave ping-pong kernel
-// (256 query rows per block) when it still gives every CU a block, else the
-// 4-wave pipelined kernel (128 rows per block, up to two blocks per CU).  At
-// d = 64 the pipelined kernel throughout: there the softmax work per tile is
-// as large as the MFMA work, and the pipelined kernel's two blocks per CU
-// measured 2-8 % faster than the ping-pong kernel on long sequences.  The
-// environment variable ATTN_FWD_KERNEL=pingpong|pipelined forces one (for
-// tests and sweeps).
-bool use_pingpong(int64_t blocks256, int64_t d) {
+// (256 query rows per block) when it still gives every CU a block and the
+// queries fill more than one 128-row block, else the 4-wave pipelined kernel
+// (128 rows per block, up to two blocks per CU).  With at most 128 query rows
+// a 256-row block would be half padding or more: a split-KV call of 8 or 16
+// rows against 65536 keys (B1 H32) measured 184 us with the pipelined kernel
+// against 231 us with the ping-pong kernel.  At d = 64 the pipelined kernel
+// throughout: there the softmax work per tile is as large as the MFMA work,
+// and the pipelined kernel's two blocks per CU measured 2-8 % faster than the
+// ping-pong kernel on long sequences.  The environment variable
+// ATTN_FWD_KERNEL=pingpong|pipelined forces one (for tests and sweeps).
+bool use_pingpong(int64_t blocks256, int64_t N, int64_t d) {
   const char* env = getenv("ATTN_FWD_KERNEL");
   if (env != nullptr && strcmp(env, "pingpong") == 0) return true;
   if (env != nullptr && (strcmp(env, "pipelined") == 0 || strcmp(env, "pipelined2") == 0))
     return false;
-  return d == 128 && blocks256 >= kNumCUs;
+  return d == 128 && N > 128 && blocks256 >= kNumCUs;
 }
 
 // The pipelined kernel's in-block key split: when the grid of 128-row blocks
@@ -1766,7 +1769,7 @@ int launch_dec(const Launch& a) {
 template <class E, class T, bool C>
 int launch16(const Launch& a) {
   if (use_decode(a.N, C)) return launch_dec<E, T>(a);
-  if (use_pingpong(a.bh * ((a.N + 255) / 256) * a.splits, a.d)) {
+  if (use_pingpong(a.bh * ((a.N + 255) / 256) * a.splits, a.N, a.d)) {
     const int64_t nqt = (a.N + 255) / 256;
     auto kern = a.d == 128 ? attn_fwd_pp16<E, 128, C> : attn_fwd_pp16<E, 64, C>;
     return launch<T>(kern, a.bh * nqt, kPPThreads, (int)nqt, a);

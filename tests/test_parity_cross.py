@@ -8,7 +8,8 @@ names it the bandwidth-bound case of inference).  The cases cover one query
 against short, ragged and long key sets, a few queries against many keys, many
 queries against few keys, every kernel the library can pick for the 16-bit
 types (up to four query rows go to the decode kernel, which streams K and V
-with plain loads and computes on the VALU), the split-KV path (with a workspace and with the library's static
+with plain loads and computes on the VALU; up to 128 rows to the pipelined
+kernel), the split-KV path (with a workspace and with the library's static
 one), the [B, N, H, d] layout, hot keys, and the decode workload whole
 (B=1, H=32, one query against 65536 keys, d=128, bf16, in the launch
 configuration bench.py times).  Every element of O and lse is compared with
@@ -113,7 +114,32 @@ def test_cross_lengths_scale_of_either_sign():
     _compare("f32", 128, 1, 2, 9, 1111, seed=602, scale=0.4, what="scale 0.4")
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 4])
+SMALL_N = [(5, 1), (5, 63), (16, 64), (31, 65), (32, 257), (33, 4000), (64, 1111), (40, 200)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [0, 5])
+@pytest.mark.parametrize("N,Nk", SMALL_N, ids=[f"N{a}-Nk{b}" for a, b in SMALL_N])
+def test_few_query_rows(dtype, d, splits, N, Nk):
+    """5 to 64 query rows (the pipelined kernel's 128-row blocks, whatever
+    the grid), with and without key splits, hot keys."""
+    _compare(dtype, d, 2, 2, N, Nk, seed=1000 + N + Nk + d, splits=splits, hot=True,
+             what=f"few rows {dtype} d{d} N{N} Nk{Nk} S{splits}")
+
+
+@pytest.mark.parametrize("key", [10, 70, 130, 200])
+def test_few_rows_nan_key_poisons_its_head_only(key):
+    """A NaN key anywhere in a head's keys (four different 64-key tiles)
+    reaches every output row of that head and no other."""
+    q, k, v = datagen.make_qkv_kv(1, 2, 20, 256, 128, "bf16", 1100 + key)
+    k[0, 1, key, 3] = float("nan")
+    o, lse = _run(q, k, v, 0.088)
+    assert np.all(np.isnan(o[0, 1])) and np.all(np.isnan(lse[0, 1]))
+    assert np.all(np.isfinite(o[0, 0])) and np.all(np.isfinite(lse[0, 0]))
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 20])
 def test_decode_kernel_is_deterministic(N):
     """The same inputs give the same bits, with and without key splits."""
     attn = _attn()

@@ -1717,17 +1717,22 @@ constexpr int kNumCUs = 256;  // MI355X
 // (128 rows per block, up to two blocks per CU).  With at most 128 query rows
 // a 256-row block would be half padding or more: a split-KV call of 8 or 16
 // rows against 65536 keys (B1 H32) measured 184 us with the pipelined kernel
-// against 231 us with the ping-pong kernel.  At d = 64 the pipelined kernel
-// throughout: there the softmax work per tile is as large as the MFMA work,
-// and the pipelined kernel's two blocks per CU measured 2-8 % faster than the
-// ping-pong kernel on long sequences.  The environment variable
+// against 231 us with the ping-pong kernel.  At d = 64, where the softmax
+// work per tile is as large as the MFMA work, the pipelined kernel with up to
+// three blocks per CU wins on large grids (workload B1 H8 N65536: 2-8 %),
+// but while the grid gives each CU one or two 256-row blocks (two to four
+// 128-row ones) the ping-pong kernel's 8 waves per block measured 3-10 %
+// faster (B1 H32 N2048: 41.0 against 45.0 us; B1 H16 N4096: 78.2 against
+// 84.0; B1 H64 N1024: 23.3 against 25.1), so there it runs at d = 64 too
+// (without a causal mask, the case measured).  The environment variable
 // ATTN_FWD_KERNEL=pingpong|pipelined forces one (for tests and sweeps).
-bool use_pingpong(int64_t blocks256, int64_t N, int64_t d) {
+bool use_pingpong(int64_t blocks256, int64_t N, int64_t d, bool causal) {
   const char* env = getenv("ATTN_FWD_KERNEL");
   if (env != nullptr && strcmp(env, "pingpong") == 0) return true;
   if (env != nullptr && (strcmp(env, "pipelined") == 0 || strcmp(env, "pipelined2") == 0))
     return false;
-  return d == 128 && N > 128 && blocks256 >= kNumCUs;
+  if (N <= 128 || blocks256 < kNumCUs) return false;
+  return d == 128 || (!causal && blocks256 <= 2 * kNumCUs);
 }
 
 // The pipelined kernel's in-block key split: when the grid of 128-row blocks
@@ -1769,7 +1774,7 @@ int launch_dec(const Launch& a) {
 template <class E, class T, bool C>
 int launch16(const Launch& a) {
   if (use_decode(a.N, C)) return launch_dec<E, T>(a);
-  if (use_pingpong(a.bh * ((a.N + 255) / 256) * a.splits, a.N, a.d)) {
+  if (use_pingpong(a.bh * ((a.N + 255) / 256) * a.splits, a.N, a.d, C)) {
     const int64_t nqt = (a.N + 255) / 256;
     auto kern = a.d == 128 ? attn_fwd_pp16<E, 128, C> : attn_fwd_pp16<E, 64, C>;
     return launch<T>(kern, a.bh * nqt, kPPThreads, (int)nqt, a);

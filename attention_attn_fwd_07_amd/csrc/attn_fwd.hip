@@ -1723,16 +1723,23 @@ constexpr int kNumCUs = 256;  // MI355X
 // but while the grid gives each CU one or two 256-row blocks (two to four
 // 128-row ones) the ping-pong kernel's 8 waves per block measured 3-10 %
 // faster (B1 H32 N2048: 41.0 against 45.0 us; B1 H16 N4096: 78.2 against
-// 84.0; B1 H64 N1024: 23.3 against 25.1), so there it runs at d = 64 too
-// (without a causal mask, the case measured).  The environment variable
-// ATTN_FWD_KERNEL=pingpong|pipelined forces one (for tests and sweeps).
+// 84.0; B1 H64 N1024: 23.3 against 25.1), so there it runs at d = 64 too.
+// With a causal mask the blocks' work grows with their query tile, and the
+// pipelined kernel's 128-row blocks balance it better: 15-19 % faster on
+// grids of one 256-row block per CU (B1 H16 N4096 d128: 99.3 against 114.3
+// us), 1-10 % on most larger ones; the ping-pong kernel keeps long causal
+// rows on grids of two 256-row blocks per CU (B2 H16 N4096: 150.3 against
+// 156.1 us), and is not used for causal rows at d = 64.  The environment
+// variable ATTN_FWD_KERNEL=pingpong|pipelined forces one (for tests and
+// sweeps).
 bool use_pingpong(int64_t blocks256, int64_t N, int64_t d, bool causal) {
   const char* env = getenv("ATTN_FWD_KERNEL");
   if (env != nullptr && strcmp(env, "pingpong") == 0) return true;
   if (env != nullptr && (strcmp(env, "pipelined") == 0 || strcmp(env, "pipelined2") == 0))
     return false;
   if (N <= 128 || blocks256 < kNumCUs) return false;
-  return d == 128 || (!causal && blocks256 <= 2 * kNumCUs);
+  if (causal) return d == 128 && N >= 4096 && blocks256 > kNumCUs && blocks256 <= 2 * kNumCUs;
+  return d == 128 || blocks256 <= 2 * kNumCUs;
 }
 
 // The pipelined kernel's in-block key split: when the grid of 128-row blocks

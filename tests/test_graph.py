@@ -116,11 +116,11 @@ def test_decode_splitkv_graph_replays():
         assert torch.equal(lse_g, lse), f"replay {r}: lse differs from the eager call"
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_backward_graph_replays(causal):
+@pytest.mark.parametrize("dtype,causal", [("bf16", False), ("bf16", True), ("f32", True)])
+def test_backward_graph_replays(dtype, causal):
     B, H, N, d = 1, 2, 260, 64
-    q, k, v = _inputs(13, B, H, N, d, "bf16")
-    do = datagen.make_grad(B, H, N, d, "bf16", 14).to("cuda")
+    q, k, v = _inputs(13, B, H, N, d, dtype)
+    do = datagen.make_grad(B, H, N, d, dtype, 14).to("cuda")
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
@@ -138,7 +138,7 @@ def test_backward_graph_replays(causal):
     with torch.cuda.graph(g):
         step()
     for r in range(REPLAYS):
-        _refill((q, k, v, do), 300 + r, "bf16")
+        _refill((q, k, v, do), 300 + r, dtype)
         g.replay()
         torch.cuda.synchronize()
         got = [t.clone() for t in (o, lse, dq, dk, dv)]
@@ -148,3 +148,44 @@ def test_backward_graph_replays(causal):
         torch.cuda.synchronize()
         for name, a, b in zip(("O", "lse", "dQ", "dK", "dV"), got, (o, lse, dq, dk, dv)):
             assert torch.equal(a, b), f"replay {r}: {name} differs from the eager call"
+
+
+def test_merge_graph_replays():
+    """Forwards over three key shards and their merge (attn_fwd_merge),
+    captured together and replayed."""
+    B, H, N, Nk, d = 1, 3, 40, 900, 128
+    q, k, v = (t.to("cuda") for t in datagen.make_qkv_kv(B, H, N, Nk, d, "bf16", 15))
+    shards = [(0, 250), (250, 700), (700, 900)]
+    ks = [k[:, :, a:b].contiguous() for a, b in shards]
+    vs = [v[:, :, a:b].contiguous() for a, b in shards]
+    parts = [(torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device="cuda"))
+             for _ in shards]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    scale = d ** -0.5
+
+    def step():
+        for kk, vv, (po, pl) in zip(ks, vs, parts):
+            aa.attn_fwd(q, kk, vv, po, pl, scale)
+        aa.merge([p[0] for p in parts], [p[1] for p in parts], o, lse)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(REPLAYS):
+        fq, fk, fv = datagen.make_qkv_kv(B, H, N, Nk, d, "bf16", 400 + r)
+        q.copy_(fq.to("cuda"))
+        for (a, b), kk, vv in zip(shards, ks, vs):
+            kk.copy_(fk[:, :, a:b].to("cuda"))
+            vv.copy_(fv[:, :, a:b].to("cuda"))
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, lse_g = o.clone(), lse.clone()
+        o.zero_()
+        lse.zero_()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o), f"replay {r}: O differs from the eager call"
+        assert torch.equal(lse_g, lse), f"replay {r}: lse differs from the eager call"

@@ -16,7 +16,8 @@
 //             the workspace for dkdv, then loops over key tiles and
 //             accumulates dQ^T = K^T dS^T in registers (the forward's
 //             layout: lane l owns query row l % 32 of its wave);
-//   * dkdv:   one block = 256 keys (8 waves); it loops over query tiles and
+//   * dkdv:   one block = 256 keys (8 waves; 128 keys and 4 waves when that
+//             leaves CUs without a block); it loops over query tiles and
 //             accumulates dK^T = Q^T dS and dV^T = dO^T P (the transposed
 //             layout: lane l owns key l % 32 of its wave).
 // Each gradient row is owned by exactly one lane pair, so there are no
@@ -404,7 +405,8 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
 // --- dK, dV ------------------------------------------------------------------
 //
-// Block: 8 waves, keys kt*256 + 32 w + (l % 32).  K rows stay in registers
+// Block: KW = 8 waves (4 on grids too small to give every CU a block of 8),
+// keys kt*32KW + 32 w + (l % 32).  K rows stay in registers
 // (the B operand of S); the block's V rows are staged once in LDS and read
 // back as the B operand of dP, which keeps a wave at no more than 256 VGPRs
 // (two waves per SIMD, one block per CU): the resident state is K (D/4
@@ -413,17 +415,17 @@ void attn_bwd_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 //   S = Q K^T and dP = dO V^T      (A from Q / dO rows),
 //   P = 2^(S c2 - lse log2 e), dS = P (dP - D) per element (lane = key),
 //   dV^T += dO^T P, dK^T += Q^T dS (A from dO / Q transposed, B = P / dS).
-constexpr int kKW = 8;             // waves of a dK/dV block
-constexpr int kBK = 32 * kKW;      // keys per dK/dV block
+constexpr int kKW = 8;             // waves of a dK/dV block (4 on small grids)
 
-template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kKW) __attribute__((amdgpu_waves_per_eu(2)))
+template <class E, int D, bool CAUSAL, int KW = kKW>
+__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const float2* __restrict__ stats,
                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nkt,
                    float c2, float scale) {
-  using G = Geo16<D, kKW>;
+  constexpr int kBK = 32 * KW;  // keys per block
+  using G = Geo16<D, KW>;
   constexpr int TB = G::TILEB, KS = D / 16, DB = D / 32;
   constexpr int VT = kBK / kBN;  // V tiles of the block
   // two buffers of (Q tile, dO tile), the block's V rows, then two buffers
@@ -445,7 +447,7 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int t0 = CAUSAL ? k0 / kBN : 0;
   const int T = (N + kBN - 1) / kBN;
 
-  const RowLoader<D, kBN, kKW> loader(__builtin_amdgcn_readfirstlane(wave));
+  const RowLoader<D, kBN, KW> loader(__builtin_amdgcn_readfirstlane(wave));
   auto load = [&](int t, int buf) __attribute__((always_inline)) {
     loader.load(Qb, t * kBN, N, lsm + (2 * buf) * TB);
     loader.load(dOb, t * kBN, N, lsm + (2 * buf + 1) * TB);
@@ -787,10 +789,20 @@ int launch_bwd(const attn_bwd_args_t& a, float2* stats, int64_t bh) {
                      dout, static_cast<const uint16_t*>(a.o), a.lse, stats,
                      static_cast<uint16_t*>(a.dq), (int)a.N, (int)nt, c2, a.scale);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
-  const int64_t nkt = (a.N + kBK - 1) / kBK;
-  hipLaunchKernelGGL((attn_bwd_dkdv<E, D, C>), dim3((unsigned)(bh * nkt)), dim3(64 * kKW), 0, s,
-                     q, k, v, dout, stats, static_cast<uint16_t*>(a.dk),
-                     static_cast<uint16_t*>(a.dv), (int)a.N, (int)nkt, c2, a.scale);
+  // dK, dV: blocks of 8 waves (256 keys) when that gives every CU a block,
+  // else of 4 waves (128 keys), twice the blocks
+  const int64_t nkt8 = (a.N + 32 * kKW - 1) / (32 * kKW);
+  if (bh * nkt8 >= 256) {
+    hipLaunchKernelGGL((attn_bwd_dkdv<E, D, C, kKW>), dim3((unsigned)(bh * nkt8)),
+                       dim3(64 * kKW), 0, s, q, k, v, dout, stats,
+                       static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), (int)a.N,
+                       (int)nkt8, c2, a.scale);
+  } else {
+    const int64_t nkt4 = (a.N + 127) / 128;
+    hipLaunchKernelGGL((attn_bwd_dkdv<E, D, C, 4>), dim3((unsigned)(bh * nkt4)), dim3(256), 0,
+                       s, q, k, v, dout, stats, static_cast<uint16_t*>(a.dk),
+                       static_cast<uint16_t*>(a.dv), (int)a.N, (int)nkt4, c2, a.scale);
+  }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

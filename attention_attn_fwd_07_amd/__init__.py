@@ -21,8 +21,9 @@ long key/value history), q, o and lse keep N.  The head dimension must be
 contiguous, the other three dimensions may have any strides that are multiples
 of 8 elements (so a ``[B, N, H, d]`` tensor viewed with ``.transpose(1, 2)`` is
 accepted without a copy).  ``lse`` is ``[B, H, N]`` fp32 contiguous (or None).
-``causal=True`` (only with Nk = N) restricts query row i to keys 0..i.  Argument errors raise ValueError, mirroring a wrapper that checks
-device, shape, dtype and layout before it launches anything (page 2 "Triton
+``causal=True`` (only with Nk = N) restricts query row i to keys 0..i.
+Argument errors raise ValueError, mirroring a wrapper that checks device,
+shape, dtype and layout before it launches anything (page 2 "Triton
 programming template", Python wrapper).
 """
 from __future__ import annotations
@@ -366,8 +367,10 @@ def merge(o_parts, lse_parts, o=None, lse=None, stream=None):
     if len(o_parts) != len(lse_parts) or not o_parts:
         raise ValueError("o_parts and lse_parts must be non-empty and of equal length")
     o0 = o_parts[0]
-    if o0.dtype not in codes or o0.dim() != 4:
+    if not isinstance(o0, torch.Tensor) or o0.dtype not in codes or o0.dim() != 4:
         raise ValueError("each part's O must be a 4-D float32/float16/bfloat16 tensor")
+    if o0.device.type != "cuda":
+        raise ValueError("the parts must be GPU tensors")
     for x, l in zip(o_parts, lse_parts):
         if (x.shape != o0.shape or x.dtype != o0.dtype or x.device != o0.device
                 or not x.is_contiguous()):
@@ -380,8 +383,13 @@ def merge(o_parts, lse_parts, o=None, lse=None, stream=None):
         o = torch.empty_like(o0)
     if lse is None:
         lse = torch.empty(o0.shape[:3], dtype=torch.float32, device=o0.device)
-    if o.shape != o0.shape or o.dtype != o0.dtype or not o.is_contiguous():
-        raise ValueError("o must be contiguous with the parts' shape and dtype")
+    if (not isinstance(o, torch.Tensor) or o.shape != o0.shape or o.dtype != o0.dtype
+            or o.device != o0.device or not o.is_contiguous()):
+        raise ValueError("o must be contiguous with the parts' shape, dtype and device")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
+            or tuple(lse.shape) != tuple(o0.shape[:3]) or lse.device != o0.device
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on the parts' device")
     if stream is None:
         stream = torch.cuda.current_stream(o0.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):

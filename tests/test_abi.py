@@ -446,3 +446,14 @@ def test_bwd_null_args(lib):
     lib.attn_bwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     lib.attn_bwd.restype = ctypes.c_int
     assert lib.attn_bwd(None, W, 1 << 20) == NULLPTR
+
+
+def test_merge_binding_rejects_host_tensors():
+    """The merge binding checks the device before any pointer reaches the
+    library (a host pointer would reach a kernel)."""
+    import torch
+    import attention_attn_fwd_07_amd as attn
+    o = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        attn.merge([o], [lse])

@@ -119,3 +119,9 @@ def test_merge_binding_rejects_bad_parts():
         attn.merge([o] * 65, [lse] * 65)                  # more parts than ATTN_MAX_SPLITS
     with pytest.raises(ValueError):
         attn.merge([o], [lse], o=o)                       # output aliases a part
+    with pytest.raises(ValueError):
+        attn.merge([o.cpu()], [lse.cpu()])                # host tensors
+    with pytest.raises(ValueError):
+        attn.merge([o], [lse], o=torch.empty_like(o).cpu())  # output on the host
+    with pytest.raises(ValueError):
+        attn.merge([o], [lse], lse=torch.empty(1, 1, 8, device=DEV, dtype=torch.float16))

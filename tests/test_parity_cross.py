@@ -206,3 +206,37 @@ def test_decode_workload_whole():
     v64 = v.double().numpy()
     assert np.all(o >= v64.min(axis=2, keepdims=True) - 2e-2)
     assert np.all(o <= v64.max(axis=2, keepdims=True) + 2e-2)
+
+
+NRANDOM = 60
+
+
+def _random_case(i):
+    rng = np.random.default_rng(9500 + i)
+    dtype = ["bf16", "f16", "f32"][int(rng.integers(3))]
+    d = [64, 128][int(rng.integers(2))]
+    N = int(np.exp(rng.uniform(0.0, np.log(600.0))))
+    Nk = int(np.exp(rng.uniform(0.0, np.log(9000.0))))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    splits = [0, 0, 2, 7, 16, 64][int(rng.integers(6))]
+    bshd = bool(rng.integers(2))
+    scale = float(np.float32(1.0 / np.sqrt(d))) if rng.random() < 0.6 else float(rng.uniform(-0.3, 0.4))
+    hot = dtype != "f32" and rng.random() < 0.3
+    return dict(dtype=dtype, d=d, N=N, Nk=Nk, B=B, H=H, splits=splits, bshd=bshd, scale=scale,
+                hot=hot, seed=9500 + i)
+
+
+def _random_id(i):
+    c = _random_case(i)
+    return (f"{i}-{c['dtype']}-d{c['d']}-N{c['N']}-Nk{c['Nk']}-B{c['B']}H{c['H']}-S{c['splits']}"
+            f"{'-bshd' if c['bshd'] else ''}{'-hot' if c['hot'] else ''}")
+
+
+@pytest.mark.parametrize("i", range(NRANDOM), ids=[_random_id(i) for i in range(NRANDOM)])
+def test_cross_lengths_random(i):
+    """A seeded sweep over dtype, head dim, N (log-uniform 1-600), Nk
+    (log-uniform 1-9000), B, H, key splits, layout, scale and hot keys; the
+    library picks the kernel (decode, pipelined or ping-pong)."""
+    c = _random_case(i)
+    _compare(c["dtype"], c["d"], c["B"], c["H"], c["N"], c["Nk"], c["seed"], scale=c["scale"],
+             splits=c["splits"], bshd=c["bshd"], hot=c["hot"], what=_random_id(i))

@@ -941,13 +941,18 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       l += softmax16<E, false>(sc, m, c2, pb, 0, 0);
     }
   };
+  // A tile that crosses the wave's causal diagonal (the max test).
+  auto valu_diag = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * G::BN;
+    mask_tail16(sc, j0, kl.lane_lim, c2);
+    maybe_rescale<D>(tile_max16(sc, c2), m, l, acc, kRescaleThreshold);
+    l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+  };
   auto valu_any = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * G::BN;
     if (kl.partial(j0, G::BN)) {
       if (CAUSAL) {
-        mask_tail16(sc, j0, kl.lane_lim, c2);
-        maybe_rescale<D>(tile_max16(sc, c2), m, l, acc, kRescaleThreshold);
-        l += softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
+        valu_diag(t);
         return;
       }
       f32x2 ps = softmax16<E, true>(sc, m, c2, pb, j0, kl.lane_lim);
@@ -962,14 +967,14 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       valu_full(t);
     }
   };
-  // Tiles between the first and the last: all full without a causal mask;
-  // with one, the block's last tiles cross the diagonal.
-  auto valu_mid = [&](int t) __attribute__((always_inline)) {
-    if (CAUSAL)
-      valu_any(t);
-    else
-      valu_full(t);
-  };
+  // Tiles between the first and the last run in two stretches: 1 .. tmid-1,
+  // which every row of the wave sees whole (the unmasked VALU phase, the
+  // whole stretch without a causal mask), then tmid .. T-2, which with a
+  // causal mask cross the wave's diagonal.  Keeping the diagonal tiles out
+  // of the main loop keeps their masking code out of its register
+  // allocation and schedule.  The stretches differ between waves, but every
+  // wave runs T-2 iterations in all, so the barrier count is the same.
+  const int tmid = CAUSAL ? min(T - 1, max(1, (kl.wave_lim + 1) / G::BN)) : T - 1;
   auto pv_last = [&]() __attribute__((always_inline)) {
     uint32_t vq = ln.vq;
     __asm__ volatile("" : "+v"(vq));
@@ -984,10 +989,15 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // tile t, await V_t.
     block_barrier(); mfma_tile(0); if (2 < T) load_tile(2);
     block_barrier(); valu_first(); wait_tile(0);
-    for (int t = 1; t < T - 1; ++t) {
+    for (int t = 1; t < tmid; ++t) {
       block_barrier(); mfma_tile(t); if (t + 2 < T) load_tile(t + 2);
-      block_barrier(); valu_mid(t); wait_tile(t);
+      block_barrier(); valu_full(t); wait_tile(t);
     }
+    if (CAUSAL)
+      for (int t = tmid; t < T - 1; ++t) {
+        block_barrier(); mfma_tile(t); if (t + 2 < T) load_tile(t + 2);
+        block_barrier(); valu_diag(t); wait_tile(t);
+      }
     if (T > 1) {
       block_barrier(); mfma_tile(T - 1);
       block_barrier(); valu_any(T - 1); wait_tile(T - 1);
@@ -1000,10 +1010,15 @@ void attn_fwd_pp16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     block_barrier();  // slot 0
     block_barrier(); mfma_tile(0); if (3 < T) load_tile(3); wait_tile(1);
     block_barrier(); valu_first();
-    for (int t = 1; t < T - 1; ++t) {
+    for (int t = 1; t < tmid; ++t) {
       block_barrier(); mfma_tile(t); if (t + 3 < T) load_tile(t + 3); wait_tile(t + 1);
-      block_barrier(); valu_mid(t);
+      block_barrier(); valu_full(t);
     }
+    if (CAUSAL)
+      for (int t = tmid; t < T - 1; ++t) {
+        block_barrier(); mfma_tile(t); if (t + 3 < T) load_tile(t + 3); wait_tile(t + 1);
+        block_barrier(); valu_diag(t);
+      }
     if (T > 1) {
       block_barrier(); mfma_tile(T - 1); wait_tile(T);
       block_barrier(); valu_any(T - 1);
@@ -1724,21 +1739,20 @@ constexpr int kNumCUs = 256;  // MI355X
 // 128-row ones) the ping-pong kernel's 8 waves per block measured 3-10 %
 // faster (B1 H32 N2048: 41.0 against 45.0 us; B1 H16 N4096: 78.2 against
 // 84.0; B1 H64 N1024: 23.3 against 25.1), so there it runs at d = 64 too.
-// With a causal mask the blocks' work grows with their query tile, and the
-// pipelined kernel's 128-row blocks balance it better: 15-19 % faster on
-// grids of one 256-row block per CU (B1 H16 N4096 d128: 99.3 against 114.3
-// us), 1-10 % on most larger ones; the ping-pong kernel keeps long causal
-// rows on grids of two 256-row blocks per CU (B2 H16 N4096: 150.3 against
-// 156.1 us), and is not used for causal rows at d = 64.  The environment
-// variable ATTN_FWD_KERNEL=pingpong|pipelined forces one (for tests and
-// sweeps).
+// With a causal mask at d = 128 the ping-pong kernel wins from N = 2048 on
+// (B2 H16 N4096: 134.6 against 155.6 us; B1 H32 N16384: 1879 against 2162;
+// B1 H16 N4096, one block per CU: 95.0 against 98.8), the pipelined kernel
+// up to N = 1024 (B1 H256 N1024: 109.7 against 112.1), where the diagonal
+// tiles are a large share of the work; at d = 64 the pipelined kernel is
+// 4-15 % faster on every causal shape tried.  The environment variable
+// ATTN_FWD_KERNEL=pingpong|pipelined forces one (for tests and sweeps).
 bool use_pingpong(int64_t blocks256, int64_t N, int64_t d, bool causal) {
   const char* env = getenv("ATTN_FWD_KERNEL");
   if (env != nullptr && strcmp(env, "pingpong") == 0) return true;
   if (env != nullptr && (strcmp(env, "pipelined") == 0 || strcmp(env, "pipelined2") == 0))
     return false;
   if (N <= 128 || blocks256 < kNumCUs) return false;
-  if (causal) return d == 128 && N >= 4096 && blocks256 > kNumCUs && blocks256 <= 2 * kNumCUs;
+  if (causal) return d == 128 && N >= 2048;
   return d == 128 || blocks256 <= 2 * kNumCUs;
 }
 

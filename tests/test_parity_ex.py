@@ -58,6 +58,19 @@ def test_causal_16bit(kernel, dtype, d, N, monkeypatch):
     causal_parity(q, k, v, 1.0 / math.sqrt(d), dtype, f"causal {kernel} {dtype} d={d} N={N}")
 
 
+@pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("N", [1000, 2100])
+def test_causal_long_rows(kernel, dtype, d, N, monkeypatch):
+    """Rows long enough that the waves of a 256-row block run a stretch of
+    tiles they see whole before the tiles that cross their diagonal (the
+    ping-pong kernel takes the two stretches in separate loops), over several
+    query blocks per head and a ragged last block."""
+    monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
+    q, k, v = datagen.make_qkv(1, 2, N, d, dtype, seed=310 + N + d)
+    causal_parity(q, k, v, 1.0 / math.sqrt(d), dtype, f"causal long {kernel} {dtype} d={d} N={N}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 31, 33, 128, 129, 300])
 def test_causal_f32(d, N):
@@ -72,11 +85,12 @@ def test_causal_large_grid():
 
 
 @pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])
-def test_causal_hot_keys_and_negative_scale(kernel, monkeypatch):
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_hot_keys_and_negative_scale(kernel, d, monkeypatch):
     monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
-    q, k, v = datagen.make_qkv(1, 2, 1500, 64, "bf16", seed=57, hot_frac=0.01, hot_mult=8.0)
-    causal_parity(q, k, v, 0.125, "bf16", f"causal hot keys {kernel}")
-    causal_parity(q, k, v, -0.125, "bf16", f"causal negative scale {kernel}")
+    q, k, v = datagen.make_qkv(1, 2, 1500, d, "bf16", seed=57, hot_frac=0.01, hot_mult=8.0)
+    causal_parity(q, k, v, 0.125, "bf16", f"causal hot keys {kernel} d={d}")
+    causal_parity(q, k, v, -0.125, "bf16", f"causal negative scale {kernel} d={d}")
 
 
 @pytest.mark.parametrize("kernel", ["pingpong", "pipelined"])

@@ -10,7 +10,9 @@ workload is B=2, H=16, N=4096, d=128 bf16 (the 4096-length case whose
 4096x4096 score matrix must never be materialised); ``--workload`` selects any
 of the five synthetic workloads.
 
-Timing: W untimed warmup launches, then exactly K launches back to back on
+Timing: with --warmup W, first --settle seconds (0.25 by default) of untimed
+back-to-back launches, then W untimed warmup launches; without it, the
+automatic warmup below.  Then exactly K launches back to back on
 torch's current stream, bracketed by torch.cuda.synchronize() on both sides
 (wall clock for ms_per_step) and by two HIP events recorded on that same
 stream just before the first and just after the last launch (mean kernel
@@ -35,7 +37,8 @@ driver reports (the current level of sysfs pp_dpm_sclk) and the socket power
 at that clock (the spec peaks are quoted at 2.4 GHz).  From an idle GPU the
 throughput takes some 25 ms of back-to-back launches to settle, hence the
 defaults: at least 0.3 s of warmup launches, then about 1 s of timed ones
-(both at least 200; --warmup and --steps set exact counts).
+(both at least 200; --warmup and --steps set exact counts, and an explicit
+--warmup count is preceded by the settle phase, reported as ``settle``).
 """
 from __future__ import annotations
 
@@ -298,13 +301,21 @@ def auto_warmup(launch, min_launches: int, min_seconds: float):
     return n, last / 20
 
 
-def timed_launches(launch, stream, steps, warmup):
+def timed_launches(launch, stream, steps, warmup, settle_s=0.0):
     """W untimed launches (``warmup``, or the automatic warmup), then exactly K
     (``steps``, or about 1 s of them, at least 200) back to back, bracketed by
     torch.cuda.synchronize() for the wall clock and by two HIP events on the
-    launch stream for the mean kernel time.  Returns (W, K, kernel ms per
-    launch, wall ms per launch, the clock sampler of the timed region)."""
+    launch stream for the mean kernel time.  With an explicit ``warmup`` count,
+    ``settle_s`` seconds of untimed back-to-back launches come first, so that
+    a short timed region does not fall inside the power manager's ramp from
+    idle (the automatic warmup is already that long).  Returns (W, K, kernel ms
+    per launch, wall ms per launch, the clock sampler of the timed region, the
+    settle phase as {"launches", "seconds"} or None)."""
     import torch
+    settle = None
+    if warmup is not None and settle_s > 0:
+        n, _ = auto_warmup(launch, min_launches=0, min_seconds=settle_s)
+        settle = {"launches": n, "seconds": settle_s}
     if warmup is not None:
         W = warmup
         t_w = time_batch(launch, W) if W > 0 else 0.0
@@ -326,7 +337,7 @@ def timed_launches(launch, stream, steps, warmup):
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    return W, K, ev0.elapsed_time(ev1) / K, wall * 1e3 / K, clock
+    return W, K, ev0.elapsed_time(ev1) / K, wall * 1e3 / K, clock, settle
 
 
 def calibrate_copy(nbytes: int, reps: int) -> None:
@@ -386,7 +397,8 @@ def run_decode(args) -> int:
     nbytes_ws = attn.splitkv_workspace_size(w["B"], w["H"], w["N"], w["d"], splits, w["Nk"])
     ws = torch.empty(max(1, nbytes_ws // 4), dtype=torch.float32, device=dev)
     launch = attn.plan(qd, kd, vd, o, lse, scale, stream, splits=splits, workspace=ws)
-    W, K, kern_ms, ms_per_step, clock = timed_launches(launch, stream, args.steps, args.warmup)
+    W, K, kern_ms, ms_per_step, clock, settle = timed_launches(launch, stream, args.steps,
+                                                               args.warmup, args.settle)
     dist = per_launch_ms(launch, stream, max(10, min(K, 50)))
     flushbuf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = per_launch_ms(launch, stream, 20, flush=lambda: flushbuf.fill_(1))
@@ -401,7 +413,7 @@ def run_decode(args) -> int:
         "metric": METRIC_DECODE,
         "value": round(value, 1),
         "unit": "GB/s",
-        "n_gpus": 1, "steps": K, "warmup": W,
+        "n_gpus": 1, "steps": K, "warmup": W, "settle": settle,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w["dtype"], "data": "synthetic",
@@ -430,6 +442,10 @@ def main(argv=None) -> int:
                     help="timed launches (default: enough for about 1 s, at least 200)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed launches first (default: about 0.3 s of them, at least 200)")
+    ap.add_argument("--settle", type=float, default=0.25, metavar="SECONDS",
+                    help="with --warmup W: untimed back-to-back launches for this long before "
+                         "the W warmup launches (from an idle GPU the throughput takes some "
+                         "25 ms of load to settle); 0 times the ramp as well")
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
@@ -448,8 +464,10 @@ def main(argv=None) -> int:
                          "flops counted as 10 B H N^2 d (the five products; N(N+1)/2 pairs "
                          "in place of N^2 when causal)")
     args = ap.parse_args(argv)
-    if (args.steps is not None and args.steps < 1) or (args.warmup is not None and args.warmup < 0):
-        print("bench.py: --steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+    if ((args.steps is not None and args.steps < 1) or (args.warmup is not None and args.warmup < 0)
+            or not 0.0 <= args.settle <= 60.0):
+        print("bench.py: --steps must be at least 1, --warmup at least 0 and --settle in "
+              "[0, 60] seconds", file=sys.stderr)
         return 2
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -508,7 +526,8 @@ def main(argv=None) -> int:
         launch = attn.plan(qd, kd, vd, o, lse, w.scale, stream, causal=args.causal)
     if args.causal:
         mode += " causal"
-    W, K, kern_ms, ms_per_step, clock = timed_launches(launch, stream, args.steps, args.warmup)
+    W, K, kern_ms, ms_per_step, clock, settle = timed_launches(launch, stream, args.steps,
+                                                               args.warmup, args.settle)
 
     # After the timed region: the per-launch spread, and for the small
     # workloads the same with L2 and the 256 MB Infinity Cache flushed first
@@ -531,6 +550,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
+        "settle": settle,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -14,6 +14,11 @@ def test_more_than_one_gpu_is_refused(capsys):
     assert "one GPU" in capsys.readouterr().err
 
 
+def test_bad_settle_is_refused(capsys):
+    assert bench.main(["--settle", "-1"]) == 2
+    assert "--settle" in capsys.readouterr().err
+
+
 def test_workload_flops_and_bytes():
     w = datagen.WORKLOADS[3]
     assert w.flops == 4 * 2 * 16 * 4096 * 4096 * 128
@@ -64,6 +69,8 @@ def test_bench_json_line(extra, capsys):
                 "roofline"):
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    # an explicit warmup count comes after the default 0.25 s settle phase
+    assert d["settle"]["seconds"] == 0.25 and d["settle"]["launches"] >= 20
     assert d["unit"] == "TFLOP/s" and d["higher_is_better"] is True
     assert d["config"]["workload"] == datagen.WORKLOADS[2].name
     r = d["roofline"]
@@ -165,6 +172,7 @@ def test_bench_default_counts_are_time_based(capsys):
     assert bench.main(["--workload", "2", "--no-cpu-baseline"]) == 0
     d = json.loads([x for x in capsys.readouterr().out.splitlines() if x.strip()][-1])
     assert d["warmup"] >= 200 and d["steps"] >= 200
+    assert d["settle"] is None  # the automatic warmup is the settle phase itself
     assert d["steps"] * d["ms_per_step"] >= 500.0  # about 1 s of timed launches
     c = d["clock"]
     if c is not None:

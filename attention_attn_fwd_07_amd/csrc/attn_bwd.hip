@@ -464,17 +464,28 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // lse (log2 domain; +inf past N, so P = 0) and D of the tile's queries:
   // thread i < 128 fetches one value into a register early in an iteration
   // and stores it to LDS at its end, once the iteration's compute is issued.
+  // Whether a thread fetches lse (wave 0) or D (wave 1) is wave-uniform
+  // (kBN = 64 threads each), and so is its out-of-range default: both are
+  // formed in scalars, so that the default takes no vector register across
+  // the key loop (at d = 128 every vector register is taken, and a per-lane
+  // default was spilled to scratch and reloaded in every iteration).
+  const int swave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const float sdefault = swave == 0 ? INFINITY : 0.f;
+  static_assert(kBN == 64, "one wave per statistic");
+  const int slane = (int)(threadIdx.x & (kBN - 1));
+  // past the end the lane reads the last row (in bounds); the value is
+  // replaced by the default when it is stored, after it has arrived
   auto fetch_stat = [&](int t) __attribute__((always_inline)) -> float {
-    const int i = threadIdx.x;
-    const int q = t * kBN + (i & (kBN - 1));
-    if (i >= 2 * kBN || q >= N) return i < kBN ? INFINITY : 0.f;
-    return i < kBN ? stats[(size_t)bh * N + q].x : stats[(size_t)bh * N + q].y;
+    if (swave >= 2) return sdefault;
+    const int q = min(t * kBN + slane, N - 1);
+    return reinterpret_cast<const float*>(stats)[2 * ((size_t)bh * N + q) + swave];
   };
-  auto store_stat = [&](float x, int buf) __attribute__((always_inline)) {
-    if (threadIdx.x < 2 * kBN) stat[buf * 2 * kBN + threadIdx.x] = x;
+  auto store_stat = [&](float x, int t, int buf) __attribute__((always_inline)) {
+    if (threadIdx.x < 2 * kBN)
+      stat[buf * 2 * kBN + threadIdx.x] = t * kBN + slane < N ? x : sdefault;
   };
   load(t0, 0);
-  store_stat(fetch_stat(t0), 0);
+  store_stat(fetch_stat(t0), t0, 0);
 
   const int key = k0 + wave * 32 + li;
   u32x4 kf[KS];
@@ -519,10 +530,14 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
       // P and dS in place of S and dP
+      // the lane's offset into the statistics, formed again each half from
+      // the thread index rather than kept live (or spilled) across the loop
+      int hh4 = (int)(threadIdx.x >> 3) & 4;
+      __asm__ volatile("" : "+v"(hh4));
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // queries 32 sb + 8 g + 4 hh .. +3 of the tile: their lse and D
-        const int qi = 32 * sb + 8 * g + 4 * hh;
+        const int qi = 32 * sb + 8 * g + hh4;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + qi);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + kBN + qi);
 #pragma unroll
@@ -549,7 +564,7 @@ void attn_bwd_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
     }
-    if (more) store_stat(nxt, buf ^ 1);
+    if (more) store_stat(nxt, t + 1, buf ^ 1);
     wait_vmcnt<0>();
     __syncthreads();
   }
